@@ -1,0 +1,306 @@
+"""Pins for the fp64 oracle, against facts other than the oracle itself.
+
+Each check is a plain function raising AssertionError, so the mutation tests
+at the bottom can plant a mistake in the oracle (on the CPU) and confirm that
+some pin catches it.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention as A
+
+RNG = np.random.default_rng(20240601)
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand(*shape, scale=1.0, rng=None):
+    return (rng or RNG).standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------- pin checks
+def check_rows_sum_to_one():
+    q, k, v = rand(2, 4, 37, 16), rand(2, 2, 45, 16), rand(2, 2, 45, 16)
+    lens = np.array([45, 13])
+    for causal in (False, True):
+        P = oracle.attention_probs_ref(q, k, v, causal=causal, kv_seqlens=lens, scale=0.3125)
+        assert np.allclose(P.sum(-1), 1.0, rtol=0, atol=1e-13)
+        assert np.all(P[1, :, :, 13:] == 0.0)  # padded keys carry exactly zero weight
+        if causal:
+            i = np.arange(37)[:, None]; j = np.arange(45)[None, :]
+            assert np.all(P[0][:, j > i + 8] == 0.0)
+
+
+def check_constant_v():
+    q, k = rand(1, 3, 20, 8), rand(1, 3, 33, 8)
+    c = rand(8)
+    v = np.broadcast_to(c, (1, 3, 33, 8)).copy()
+    for causal in (False, True):
+        O, _ = oracle.attention_ref(q, k, v, causal=causal, kv_seqlens=[29], scale=0.6875)
+        assert np.allclose(O, c, rtol=0, atol=1e-13)
+
+
+def check_single_key():
+    q, k, v = rand(2, 2, 5, 8), rand(2, 2, 1, 8), rand(2, 2, 1, 8)
+    s = 0.25
+    O, L = oracle.attention_ref(q, k, v, scale=s)
+    for b in range(2):
+        for h in range(2):
+            assert np.allclose(O[b, h], v[b, h, 0], rtol=0, atol=1e-14)
+            assert np.allclose(L[b, h], s * q[b, h] @ k[b, h, 0], rtol=0, atol=1e-13)
+    # a length-1 padding mask reduces any cache to its first key
+    k2, v2 = rand(1, 1, 9, 8), rand(1, 1, 9, 8)
+    O, L = oracle.attention_ref(q[:1, :1], k2, v2, kv_seqlens=[1], scale=s)
+    assert np.allclose(O[0, 0], v2[0, 0, 0], atol=1e-14)
+    assert np.allclose(L[0, 0], s * q[0, 0] @ k2[0, 0, 0], atol=1e-13)
+
+
+def check_causal_row0():
+    q, k, v = rand(1, 2, 16, 8), rand(1, 2, 16, 8), rand(1, 2, 16, 8)
+    s = 0.375
+    O, L = oracle.attention_ref(q, k, v, causal=True, scale=s)
+    for h in range(2):
+        assert np.allclose(O[0, h, 0], v[0, h, 0], rtol=0, atol=1e-14)
+        assert abs(L[0, h, 0] - s * q[0, h, 0] @ k[0, h, 0]) < 1e-13
+        # row 1 is the two-key softmax of keys 0 and 1
+        s0, s1 = s * q[0, h, 1] @ k[0, h, 0], s * q[0, h, 1] @ k[0, h, 1]
+        w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        assert np.allclose(O[0, h, 1], w0 * v[0, h, 0] + (1 - w0) * v[0, h, 1], atol=1e-13)
+
+
+def check_zero_q_closed_form():
+    """Q = 0: every allowed score is 0, so O_i = mean of allowed V rows and
+    LSE_i = ln(#allowed keys of row i)."""
+    B, Hq, Hkv, Nq, Nk, d = 3, 4, 2, 24, 30, 8
+    q = np.zeros((B, Hq, Nq, d))
+    k, v = rand(B, Hkv, Nk, d), rand(B, Hkv, Nk, d)
+    lens = np.array([30, 7, 0])
+    for causal in (False, True):
+        O, L = oracle.attention_ref(q, k, v, causal=causal, kv_seqlens=lens, scale=0.875)
+        for b in range(B):
+            for hq in range(Hq):
+                hk = hq // 2
+                for i in range(Nq):
+                    n = lens[b] if not causal else min(lens[b], max(0, i + (Nk - Nq) + 1))
+                    if n == 0:
+                        assert np.all(O[b, hq, i] == 0) and L[b, hq, i] == -np.inf
+                    else:
+                        assert np.allclose(O[b, hq, i], v[b, hk, :n].mean(0), atol=1e-13)
+                        assert abs(L[b, hq, i] - math.log(n)) < 1e-13
+
+
+def check_two_keys():
+    q, k, v = rand(1, 1, 6, 4), rand(1, 1, 2, 4), rand(1, 1, 2, 4)
+    s = 1.25
+    O, L = oracle.attention_ref(q, k, v, scale=s)
+    for i in range(6):
+        s0, s1 = s * q[0, 0, i] @ k[0, 0, 0], s * q[0, 0, i] @ k[0, 0, 1]
+        sig = 1.0 / (1.0 + math.exp(-(s0 - s1)))
+        assert np.allclose(O[0, 0, i], sig * v[0, 0, 0] + (1 - sig) * v[0, 0, 1], atol=1e-14)
+        assert abs(L[0, 0, i] - np.logaddexp(s0, s1)) < 1e-13
+
+
+def check_blocked_recurrence():
+    """The concept note's per-block update equals the one-shot softmax."""
+    rng = np.random.default_rng(7)
+    for nq, nk, causal, L in [(17, 64, False, 64), (33, 33, True, 33), (64, 64, True, 50),
+                              (5, 61, False, 40), (12, 7, True, 7)]:
+        q, k, v = rand(1, 1, nq, 16, rng=rng), rand(1, 1, nk, 16, rng=rng), rand(1, 1, nk, 16, rng=rng)
+        O_ref, L_ref = oracle.attention_ref(q, k, v, causal=causal, kv_seqlens=[L], scale=0.5)
+        allowed = A._allowed(nq, nk, L, causal)
+        for block in (1, 3, 16, 128):
+            O, lse = oracle.online_softmax_blocked(q[0, 0], k[0, 0], v[0, 0], block, 0.5, allowed)
+            fin = np.isfinite(L_ref[0, 0])
+            assert np.allclose(O, O_ref[0, 0], rtol=0, atol=1e-12), (nq, nk, block)
+            assert np.allclose(lse[fin], L_ref[0, 0][fin], rtol=0, atol=1e-12)
+            assert np.all(lse[~fin] == -np.inf)
+
+
+def check_key_permutation():
+    q, k, v = rand(2, 3, 11, 8), rand(2, 3, 19, 8), rand(2, 3, 19, 8)
+    perm = RNG.permutation(19)
+    O1, L1 = oracle.attention_ref(q, k, v, scale=0.625)
+    O2, L2 = oracle.attention_ref(q, k[:, :, perm], v[:, :, perm], scale=0.625)
+    assert np.allclose(O1, O2, atol=1e-13) and np.allclose(L1, L2, atol=1e-13)
+
+
+def check_gqa_equals_mha():
+    q, k, v = rand(2, 8, 13, 8), rand(2, 2, 21, 8), rand(2, 2, 21, 8)
+    lens = np.array([21, 9])
+    kr, vr = np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1)
+    for causal in (False, True):
+        O1, L1 = oracle.attention_ref(q, k, v, causal=causal, kv_seqlens=lens, scale=0.5)
+        O2, L2 = oracle.attention_ref(q, kr, vr, causal=causal, kv_seqlens=lens, scale=0.5)
+        assert np.allclose(O1, O2, atol=1e-14) and np.allclose(L1, L2, atol=1e-14)
+
+
+def _torch_sdpa(q, k, v, causal, lens, scale):
+    qt, kt, vt = (torch.from_numpy(x) for x in (q, k, v))
+    Nq, Nk = q.shape[2], k.shape[2]
+    i = torch.arange(Nq)[:, None]; j = torch.arange(Nk)[None, :]
+    mask = torch.ones(q.shape[0], 1, Nq, Nk, dtype=torch.bool)
+    for b in range(q.shape[0]):
+        L = Nk if lens is None else int(lens[b])
+        mb = j < L
+        if causal:
+            mb = mb & (j <= i + (Nk - Nq))
+        mask[b, 0] = mb
+    O = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, attn_mask=mask, scale=scale, enable_gqa=True)
+    g = q.shape[1] // k.shape[1]
+    S = scale * (qt @ kt.repeat_interleave(g, dim=1).transpose(-1, -2))
+    S = S.masked_fill(~mask, float("-inf"))
+    return O.numpy(), torch.logsumexp(S, dim=-1).numpy()
+
+
+def check_against_torch_sdpa():
+    q, k, v = rand(2, 8, 40, 16), rand(2, 2, 52, 16), rand(2, 2, 52, 16)
+    lens = np.array([52, 31])
+    for causal in (False, True):
+        for ln in (None, lens):
+            O, L = oracle.attention_ref(q, k, v, causal=causal, kv_seqlens=ln, scale=0.25)
+            Ot, Lt = _torch_sdpa(q, k, v, causal, ln, 0.25)
+            assert np.allclose(O, Ot, rtol=0, atol=1e-12)
+            assert np.allclose(L, Lt, rtol=0, atol=1e-12)
+    # the library's own causal flag (top-left alignment) agrees when Nq == Nk
+    q2, k2, v2 = rand(1, 4, 33, 16), rand(1, 4, 33, 16), rand(1, 4, 33, 16)
+    O, _ = oracle.attention_ref(q2, k2, v2, causal=True, scale=0.25)
+    Ot = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.from_numpy(x) for x in (q2, k2, v2)), is_causal=True, scale=0.25).numpy()
+    assert np.allclose(O, Ot, atol=1e-12)
+
+
+def check_merge_identity():
+    q, k, v = rand(3, 8, 1, 16), rand(3, 2, 100, 16), rand(3, 2, 100, 16)
+    lens = np.array([100, 37, 0])
+    O_full, L_full = oracle.attention_ref(q, k, v, kv_seqlens=lens, scale=0.3125)
+    for S, tile in [(1, 1), (4, 8), (7, 1), (16, 16), (64, 1)]:
+        Op, Lp = oracle.decode_partials_ref(q, k, v, lens, 0.3125, S, tile)
+        O, L = oracle.merge_partials(Op, Lp)
+        assert np.allclose(O, O_full[:, :, 0], atol=1e-13), (S, tile)
+        fin = np.isfinite(L_full[:, :, 0])
+        assert np.allclose(L[fin], L_full[:, :, 0][fin], atol=1e-13) and np.all(L[~fin] == -np.inf)
+    # any chunking of the keys, including uneven chunks, merges back exactly
+    cuts = [0, 3, 40, 41, 100]
+    parts = [oracle.attention_ref(q, k[:, :, a:b], v[:, :, a:b], scale=0.3125)
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    O, L = oracle.merge_partials(np.stack([p[0] for p in parts], -2),
+                                 np.stack([p[1] for p in parts], -1))
+    O_all, L_all = oracle.attention_ref(q, k, v, scale=0.3125)
+    assert np.allclose(O, O_all, atol=1e-13) and np.allclose(L, L_all, atol=1e-13)
+
+
+def check_split_bounds():
+    for L, S, tile in [(32768, 16, 128), (3000, 16, 128), (5, 16, 128), (0, 4, 64), (100, 7, 1)]:
+        b = oracle.split_bounds(L, S, tile)
+        assert len(b) == S and b[0][0] == 0 and b[-1][1] == L
+        assert all(b[i][1] == b[i + 1][0] for i in range(S - 1))
+        assert all((a % tile == 0) or a == L for a, _ in b)
+    assert oracle.split_bounds(32768, 16, 128)[1] == (2048, 4096)
+
+
+PIN_CHECKS = [check_rows_sum_to_one, check_constant_v, check_single_key, check_causal_row0,
+              check_zero_q_closed_form, check_two_keys, check_blocked_recurrence,
+              check_key_permutation, check_gqa_equals_mha, check_against_torch_sdpa,
+              check_merge_identity, check_split_bounds]
+
+
+@pytest.mark.parametrize("check", PIN_CHECKS, ids=lambda f: f.__name__)
+def test_pin(check):
+    check()
+
+
+def test_page_sizes():
+    entries = json.load(open(os.path.join(GOLDEN, "page_sizes.json")))["entries"]
+    e0, e1, e2 = entries
+    assert oracle.score_matrix_bytes(e0["n"], e0["bytes_per_element"]) == e0["approx_bytes_mib"] * 2**20
+    assert abs(e1["n"] ** 2 - e1["approx_elements"]) / e1["approx_elements"] < 0.01
+    assert oracle.score_matrix_bytes(e1["n"], e1["bytes_per_element"]) == e1["approx_bytes_mb"] * 2**20
+    assert e2["n"] ** 2 == e2["approx_elements"]
+
+
+def test_inputs_recipe():
+    """Seeded generator: slices reproduce, bf16 rounding is RNE of the fp32 draw."""
+    from exact_tiled_attention_08_amd import inputs
+    q, k, v, lens = inputs.make_inputs(4, B=3, Hq=4, Hkv=1, Nq=64, Nk=64)
+    assert q.dtype == torch.bfloat16 and q.shape == (3, 4, 64, 128) and k.shape == (3, 1, 64, 128)
+    assert lens is not None and lens.dtype == torch.int32 and lens.shape == (3,)
+    g = torch.Generator("cpu").manual_seed(inputs.slice_seed(4, inputs.TENSOR_K, 2))
+    ref = torch.randn((1, 64, 128), generator=g).to(torch.bfloat16)
+    assert torch.equal(k[2], ref)
+    q2, _, _, _ = inputs.make_inputs(4, B=3, Hq=4, Hkv=1, Nq=64, Nk=64)
+    assert torch.equal(q, q2)
+    full_lens = inputs.lengths(4, 4, 2048, 4096)
+    assert int(full_lens.min()) >= 2048 and int(full_lens.max()) <= 4096
+
+
+# ------------------------------------------------------- planted mistakes
+def _mut_causal_off_by_one(nq, nk, length, causal):
+    i = np.arange(nq)[:, None]; j = np.arange(nk)[None, :]
+    allowed = np.broadcast_to(j < length, (nq, nk))
+    if causal:
+        allowed = allowed & (j < i + (nk - nq))
+    return allowed
+
+
+def _mut_padding_inclusive(nq, nk, length, causal):
+    i = np.arange(nq)[:, None]; j = np.arange(nk)[None, :]
+    allowed = np.broadcast_to(j <= length, (nq, nk))
+    if causal:
+        allowed = allowed & (j <= i + (nk - nq))
+    return allowed
+
+
+def _mut_head_modulo(hq, n_q_heads, n_kv_heads):
+    return hq % n_kv_heads
+
+
+def _mut_lse_drops_max(qh, kh, vh, allowed, scale):
+    O, lse, P = _ORIG_ONE_HEAD(qh, kh, vh, allowed, scale)
+    S = np.where(allowed, scale * (qh @ kh.T), -np.inf)
+    m = S.max(axis=1)
+    return O, np.where(np.isfinite(m), lse - m, lse), P
+
+
+def _mut_scale_twice(qh, kh, vh, allowed, scale):
+    return _ORIG_ONE_HEAD(qh, kh, vh, allowed, scale * scale)
+
+
+def _mut_transposed_probs(qh, kh, vh, allowed, scale):
+    O, lse, P = _ORIG_ONE_HEAD(qh, kh, vh, allowed, scale)
+    if P.shape[0] == P.shape[1]:
+        O = P.T @ vh
+    return O, lse, P
+
+
+def _mut_merge_unweighted(o_parts, lse_parts):
+    O, lse = _ORIG_MERGE(o_parts, lse_parts)
+    return np.asarray(o_parts).mean(axis=-2), lse
+
+
+_ORIG_ONE_HEAD = A._one_head
+_ORIG_MERGE = A.merge_partials
+
+MUTANTS = [("_allowed", _mut_causal_off_by_one), ("_allowed", _mut_padding_inclusive),
+           ("_head_map", _mut_head_modulo), ("_one_head", _mut_lse_drops_max),
+           ("_one_head", _mut_scale_twice), ("_one_head", _mut_transposed_probs),
+           ("merge_partials", _mut_merge_unweighted)]
+
+
+@pytest.mark.parametrize("name,mutant", MUTANTS, ids=lambda x: getattr(x, "__name__", x))
+def test_pins_catch_planted_mistake(monkeypatch, name, mutant):
+    monkeypatch.setattr(A, name, mutant)
+    if name == "merge_partials":
+        monkeypatch.setattr(oracle, "merge_partials", mutant)
+    failed = []
+    for check in PIN_CHECKS:
+        try:
+            check()
+        except AssertionError:
+            failed.append(check.__name__)
+    assert failed, f"no pin caught the planted mistake {mutant.__name__}"
