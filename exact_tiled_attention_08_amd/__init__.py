@@ -1,0 +1,183 @@
+"""Exact tiled attention (prefill forward, split-KV decode, LSE merge) on gfx950.
+
+Thin torch-facing wrappers over the C ABI in include/fa.h.  Each function has
+the name of the C entry point it marshals arguments for; all computation runs
+in the HIP kernels of libfa.so (loaded on first use, never replaced by a CPU
+path).
+"""
+import math
+
+import torch
+
+from . import _lib
+from ._lib import FAError, FA_DECODE_SPLIT_ALIGN, FA_MAX_SPLITS  # noqa: F401
+
+__all__ = ["fa_fwd", "fa_decode_splitkv", "fa_lse_merge", "fa_decode", "fa_decode_workspace_bytes",
+           "fa_status_string", "fa_last_error", "FAError", "default_scale"]
+
+_DTYPES = {torch.bfloat16: _lib.FA_BF16, torch.float32: _lib.FA_F32}
+
+
+def default_scale(d):
+    return 1.0 / math.sqrt(d)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check_tensor(t, name, dtype=None, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+
+
+def _lens(kv_seqlens, B, device):
+    if kv_seqlens is None:
+        return None
+    _check_tensor(kv_seqlens, "kv_seqlens", torch.int32, 1, device)
+    if kv_seqlens.numel() != B:
+        raise ValueError("kv_seqlens must have B entries")
+    return kv_seqlens
+
+
+def fa_fwd(q, k, v, causal=False, kv_seqlens=None, scale=None, out=None, lse=None):
+    """Exact attention forward.  q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] (bf16 or f32).
+
+    Returns (o [B,Hq,Nq,d] in q's dtype, lse [B,Hq,Nq] float32).
+    """
+    _check_tensor(q, "q", ndim=4)
+    if q.dtype not in _DTYPES:
+        raise ValueError("q must be bfloat16 or float32")
+    _check_tensor(k, "k", q.dtype, 4, q.device)
+    _check_tensor(v, "v", q.dtype, 4, q.device)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, Hkv, Nk, d] matching q")
+    lens = _lens(kv_seqlens, B, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check_tensor(out, "out", q.dtype, 4, q.device)
+    _check_tensor(lse, "lse", torch.float32, 3, q.device)
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("out/lse have the wrong shape")
+    s = default_scale(d) if scale is None else float(scale)
+    lib = _lib.load()
+    _lib.check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, s,
+                          int(bool(causal)), _ptr(lens), _DTYPES[q.dtype], _stream(q)))
+    return out, lse
+
+
+def fa_decode_workspace_bytes(B, Hq, d, num_splits):
+    return int(_lib.load().fa_decode_workspace_bytes(B, Hq, d, num_splits))
+
+
+def _decode_shapes(q, k_cache, v_cache):
+    _check_tensor(q, "q", ndim=4)
+    if q.dtype not in _DTYPES:
+        raise ValueError("q must be bfloat16 or float32")
+    _check_tensor(k_cache, "k_cache", q.dtype, 4, q.device)
+    _check_tensor(v_cache, "v_cache", q.dtype, 4, q.device)
+    B, Hq, one, d = q.shape
+    if one != 1:
+        raise ValueError("decode takes q of shape [B, Hq, 1, d]")
+    Hkv, Nk = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, Nk, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches must be [B, Hkv, Nk, d] matching q")
+    return B, Hq, Hkv, Nk, d
+
+
+def fa_decode_splitkv(q, k_cache, v_cache, num_splits=16, kv_seqlens=None, scale=None,
+                      o_part=None, lse_part=None):
+    """Split-KV decode partials: (o_part [B,Hq,S,d] f32, lse_part [B,Hq,S] f32)."""
+    B, Hq, Hkv, Nk, d = _decode_shapes(q, k_cache, v_cache)
+    lens = _lens(kv_seqlens, B, q.device)
+    if o_part is None:
+        o_part = torch.empty((B, Hq, num_splits, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, Hq, num_splits), dtype=torch.float32, device=q.device)
+    _check_tensor(o_part, "o_part", torch.float32, 4, q.device)
+    _check_tensor(lse_part, "lse_part", torch.float32, 3, q.device)
+    if tuple(o_part.shape) != (B, Hq, num_splits, d) or tuple(lse_part.shape) != (B, Hq, num_splits):
+        raise ValueError("o_part/lse_part have the wrong shape")
+    s = default_scale(d) if scale is None else float(scale)
+    lib = _lib.load()
+    _lib.check(lib.fa_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o_part), _ptr(lse_part),
+                                     B, Hq, Hkv, Nk, d, s, _ptr(lens), num_splits, _DTYPES[q.dtype],
+                                     _stream(q)))
+    return o_part, lse_part
+
+
+def fa_lse_merge(o_part, lse_part, dtype=torch.bfloat16, out=None, lse=None):
+    """Merge partials [..., S, d] / [..., S] into (o [..., 1, d] dtype, lse [..., 1] f32)."""
+    _check_tensor(o_part, "o_part", torch.float32)
+    _check_tensor(lse_part, "lse_part", torch.float32, o_part.dim() - 1, o_part.device)
+    S, d = o_part.shape[-2], o_part.shape[-1]
+    lead = tuple(o_part.shape[:-2])
+    if tuple(lse_part.shape) != lead + (S,):
+        raise ValueError("lse_part must be o_part.shape[:-1]")
+    rows = 1
+    for x in lead:
+        rows *= x
+    if out is None:
+        out = torch.empty(lead + (1, d), dtype=dtype, device=o_part.device)
+    if lse is None:
+        lse = torch.empty(lead + (1,), dtype=torch.float32, device=o_part.device)
+    _check_tensor(out, "out", dtype, device=o_part.device)
+    _check_tensor(lse, "lse", torch.float32, device=o_part.device)
+    if out.numel() != rows * d or lse.numel() != rows:
+        raise ValueError("out/lse have the wrong size")
+    lib = _lib.load()
+    _lib.check(lib.fa_lse_merge(_ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse), rows, d, S,
+                                _DTYPES[dtype], _stream(o_part)))
+    return out, lse
+
+
+def fa_decode(q, k_cache, v_cache, kv_seqlens=None, num_splits=16, scale=None, workspace=None,
+              out=None, lse=None):
+    """Single-token decode: split-KV partials then exact merge, one call.
+
+    Returns (o [B,Hq,1,d] in q's dtype, lse [B,Hq,1] float32).
+    """
+    B, Hq, Hkv, Nk, d = _decode_shapes(q, k_cache, v_cache)
+    lens = _lens(kv_seqlens, B, q.device)
+    lib = _lib.load()
+    need = int(lib.fa_decode_workspace_bytes(B, Hq, d, num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_tensor(workspace, "workspace", torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=q.device)
+    _check_tensor(out, "out", q.dtype, 4, q.device)
+    _check_tensor(lse, "lse", torch.float32, 3, q.device)
+    s = default_scale(d) if scale is None else float(scale)
+    _lib.check(lib.fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, Hq, Hkv, Nk, d,
+                             s, _ptr(lens), num_splits, _ptr(workspace), workspace.numel(),
+                             _DTYPES[q.dtype], _stream(q)))
+    return out, lse
+
+
+def fa_status_string(status):
+    return _lib.load().fa_status_string(status).decode()
+
+
+def fa_last_error():
+    return _lib.load().fa_last_error().decode()

@@ -1,0 +1,201 @@
+// C ABI of libfa.so: argument validation (before any HIP call), kernel
+// selection and launch on the caller's stream.  See include/fa.h for the
+// contract of each entry point.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "fa_launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return FA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t lse_offset(size_t part_bytes) { return (part_bytes + 255) / 256 * 256; }
+
+// Checks shared by the prefill and decode entry points.
+int check_common(int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int dtype) {
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0)
+    return fail(FA_ERR_INVALID_ARG, "sizes must be non-negative (B=%d Hq=%d Hkv=%d Nq=%d Nk=%d)", B, Hq, Hkv,
+                Nq, Nk);
+  if (dtype != FA_F32 && dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", d);
+  if (Hq > 0 && (Hkv <= 0 || Hq % Hkv != 0))
+    return fail(FA_ERR_UNSUPPORTED, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  return FA_OK;
+}
+
+int check_ptr(const void* p, size_t align, const char* name) {
+  if (p == nullptr) return fail(FA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(FA_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+  return FA_OK;
+}
+
+int check_splits(int num_splits) {
+  if (num_splits < 1 || num_splits > FA_MAX_SPLITS)
+    return fail(FA_ERR_UNSUPPORTED, "num_splits %d outside [1, %d]", num_splits, FA_MAX_SPLITS);
+  return FA_OK;
+}
+
+int check_decode_args(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int Nk, int d,
+                      float scale, int num_splits, int dtype) {
+  int st = check_common(B, Hq, Hkv, 1, Nk, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if ((st = check_splits(num_splits)) != FA_OK) return st;
+  if ((long long)Hkv * ((Hq / (Hkv > 0 ? Hkv : 1) + 31) / 32) > 65535 || B > 65535)
+    return fail(FA_ERR_UNSUPPORTED, "decode grid too large (B=%d, Hkv=%d)", B, Hkv);
+  if ((long long)B * Hq == 0) return FA_OK;
+  if ((st = check_ptr(q, 16, "q")) != FA_OK) return st;
+  if (Nk > 0) {
+    if ((st = check_ptr(k, 16, "k_cache")) != FA_OK) return st;
+    if ((st = check_ptr(v, 16, "v_cache")) != FA_OK) return st;
+  }
+  return FA_OK;
+}
+
+fa::AttnArgs make_args(const void* q, const void* k, const void* v, void* o, float* lse,
+                       const int32_t* kv_seqlens, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                       int causal, void* stream) {
+  fa::AttnArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.kv_seqlens = kv_seqlens;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.d = d;
+  a.scale = scale;
+  a.causal = causal;
+  a.stream = (hipStream_t)stream;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return 100; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    default: return "FA_UNKNOWN_STATUS";
+  }
+}
+
+const char* fa_last_error(void) { return g_last_error; }
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
+           int Nk, int d, float scale, int causal, const int32_t* kv_seqlens, int dtype, void* stream) {
+  int st = check_common(B, Hq, Hkv, Nq, Nk, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if ((long long)B * Hq * Nq == 0) return ok();  // nothing to write
+  if ((st = check_ptr(q, 16, "q")) != FA_OK) return st;
+  if ((st = check_ptr(o, 16, "o")) != FA_OK) return st;
+  if ((st = check_ptr(lse, 4, "lse")) != FA_OK) return st;
+  if (Nk > 0) {
+    if ((st = check_ptr(k, 16, "k")) != FA_OK) return st;
+    if ((st = check_ptr(v, 16, "v")) != FA_OK) return st;
+  }
+  if (kv_seqlens != nullptr && !aligned(kv_seqlens, 4))
+    return fail(FA_ERR_INVALID_ARG, "kv_seqlens is not 4-byte aligned");
+  const long long tiles = ((long long)Nq + 127) / 128 * B * Hq;
+  if (tiles > 0x7fffffffLL) return fail(FA_ERR_UNSUPPORTED, "problem too large for one launch");
+  fa::AttnArgs a = make_args(q, k, v, o, lse, kv_seqlens, B, Hq, Hkv, Nq, Nk, d, scale, causal, stream);
+  if (dtype == FA_BF16) return hip_status(fa::launch_fwd_bf16(a), "fa_fwd (bf16) launch");
+  return hip_status(fa::launch_fwd_f32(a, nullptr), "fa_fwd (f32) launch");
+}
+
+size_t fa_decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
+  if (B < 0 || Hq < 0 || (d != 64 && d != 128) || num_splits < 1 || num_splits > FA_MAX_SPLITS) return 0;
+  const size_t rows = (size_t)B * Hq * num_splits;
+  return lse_offset(rows * d * sizeof(float)) + rows * sizeof(float);
+}
+
+int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache, float* o_part, float* lse_part,
+                      int B, int Hq, int Hkv, int Nk, int d, float scale, const int32_t* kv_seqlens,
+                      int num_splits, int dtype, void* stream) {
+  int st = check_decode_args(q, k_cache, v_cache, B, Hq, Hkv, Nk, d, scale, num_splits, dtype);
+  if (st != FA_OK) return st;
+  if ((long long)B * Hq == 0) return ok();
+  if ((st = check_ptr(o_part, 16, "o_part")) != FA_OK) return st;
+  if ((st = check_ptr(lse_part, 4, "lse_part")) != FA_OK) return st;
+  if (kv_seqlens != nullptr && !aligned(kv_seqlens, 4))
+    return fail(FA_ERR_INVALID_ARG, "kv_seqlens is not 4-byte aligned");
+  fa::AttnArgs a = make_args(q, k_cache, v_cache, nullptr, nullptr, kv_seqlens, B, Hq, Hkv, 1, Nk, d, scale, 0,
+                             stream);
+  fa::PartialOut part{o_part, lse_part, num_splits};
+  if (dtype == FA_BF16) return hip_status(fa::launch_decode_splitkv_bf16(a, part), "fa_decode_splitkv launch");
+  return hip_status(fa::launch_fwd_f32(a, &part), "fa_decode_splitkv (f32) launch");
+}
+
+int fa_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse, int rows, int d,
+                 int num_splits, int dtype, void* stream) {
+  if (rows < 0) return fail(FA_ERR_INVALID_ARG, "rows must be non-negative");
+  if (dtype != FA_F32 && dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", d);
+  int st = check_splits(num_splits);
+  if (st != FA_OK) return st;
+  if (rows == 0) return ok();
+  if ((st = check_ptr(o_part, 16, "o_part")) != FA_OK) return st;
+  if ((st = check_ptr(lse_part, 4, "lse_part")) != FA_OK) return st;
+  if ((st = check_ptr(o, 16, "o")) != FA_OK) return st;
+  if ((st = check_ptr(lse, 4, "lse")) != FA_OK) return st;
+  return hip_status(fa::launch_lse_merge(o_part, lse_part, o, lse, rows, d, num_splits, dtype == FA_BF16,
+                                         (hipStream_t)stream),
+                    "fa_lse_merge launch");
+}
+
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int Hq,
+              int Hkv, int Nk, int d, float scale, const int32_t* kv_seqlens, int num_splits, void* workspace,
+              size_t workspace_bytes, int dtype, void* stream) {
+  int st = check_decode_args(q, k_cache, v_cache, B, Hq, Hkv, Nk, d, scale, num_splits, dtype);
+  if (st != FA_OK) return st;
+  if ((long long)B * Hq == 0) return ok();
+  if ((st = check_ptr(o, 16, "o")) != FA_OK) return st;
+  if ((st = check_ptr(lse, 4, "lse")) != FA_OK) return st;
+  const size_t need = fa_decode_workspace_bytes(B, Hq, d, num_splits);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if (kv_seqlens != nullptr && !aligned(kv_seqlens, 4))
+    return fail(FA_ERR_INVALID_ARG, "kv_seqlens is not 4-byte aligned");
+  const size_t rows = (size_t)B * Hq;
+  float* o_part = (float*)workspace;
+  float* lse_part = (float*)((char*)workspace + lse_offset(rows * num_splits * d * sizeof(float)));
+  fa::AttnArgs a = make_args(q, k_cache, v_cache, nullptr, nullptr, kv_seqlens, B, Hq, Hkv, 1, Nk, d, scale, 0,
+                             stream);
+  fa::PartialOut part{o_part, lse_part, num_splits};
+  hipError_t e = dtype == FA_BF16 ? fa::launch_decode_splitkv_bf16(a, part) : fa::launch_fwd_f32(a, &part);
+  if (e != hipSuccess) return hip_status(e, "fa_decode split stage launch");
+  return hip_status(fa::launch_lse_merge(o_part, lse_part, o, lse, (int)rows, d, num_splits, dtype == FA_BF16,
+                                         (hipStream_t)stream),
+                    "fa_decode merge stage launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Device-side building blocks for the gfx950 attention kernels.
+//
+// Matrix-core fragment layouts used throughout (CDNA3/CDNA4 MFMA, wave64):
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds row (l % 32), k = 8*(l/32) + t for its 8 elements t
+//     B: lane l holds col (l % 32), k = 8*(l/32) + t
+//     D: lane l holds col (l % 32), rows 8*(r/4) + 4*(l/32) + (r%4), r = 0..15
+// Because k is summed over, any consistent relabelling of k between A and B
+// leaves the product unchanged; the kernels exploit that freely.
+//
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane i receives
+// element t (t = 0..3) from the 8 bytes addressed by lane (4t + i/4) of the
+// group, at position (i % 4).  Pointing lane j of a group at row (r0 + j/4),
+// column (c0 + 4*(j%4)) of a row-major bf16 tile therefore hands lane i the
+// four values tile[r0 + t][c0 + i]: a transposed 4 x 16 block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.442695040888963407f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit; 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round two floats to bf16 (round-to-nearest-even) and pack them.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 p = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
+  uint4 u;
+  u.x = pack_bf16x2(x[0], x[1]);
+  u.y = pack_bf16x2(x[2], x[3]);
+  u.z = pack_bf16x2(x[4], x[5]);
+  u.w = pack_bf16x2(x[6], x[7]);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Transposed 4 x 16 read of a row-major bf16 tile in LDS (see header note).
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 join_bf16x8(i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ int clamp_len(const int32_t* lens, int b, int nk) {
+  if (lens == nullptr) return nk;
+  int L = lens[b];
+  return L < 0 ? 0 : (L > nk ? nk : L);
+}
+
+}  // namespace fa

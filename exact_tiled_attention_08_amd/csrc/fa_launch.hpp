@@ -1,0 +1,47 @@
+// Host-side launchers shared by the C ABI (api.cpp) and the kernel sources.
+// Arguments reaching these functions have already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* kv_seqlens;
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+  hipStream_t stream;
+};
+
+struct PartialOut {
+  float* o_part;    // [B, Hq, S, d]
+  float* lse_part;  // [B, Hq, S]
+  int num_splits;   // S
+};
+
+// bf16 prefill forward on matrix cores.
+hipError_t launch_fwd_bf16(const AttnArgs& a);
+// float32 forward; with part != nullptr it computes split-KV partials instead
+// of the final output (single-token decode in float32).
+hipError_t launch_fwd_f32(const AttnArgs& a, const PartialOut* part);
+// bf16 split-KV decode partials on matrix cores (Nq == 1).
+hipError_t launch_decode_splitkv_bf16(const AttnArgs& a, const PartialOut& part);
+// Exact log-sum-exp merge of split partials into o (bf16 or f32) and lse.
+hipError_t launch_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
+                            int rows, int d, int num_splits, bool out_bf16, hipStream_t stream);
+
+// Split-KV chunk length for a sequence of `len` valid keys.
+__host__ __device__ inline int split_chunk(int len, int num_splits, int align) {
+  if (len <= 0) return 0;
+  int c = (len + num_splits - 1) / num_splits;
+  return (c + align - 1) / align * align;
+}
+
+}  // namespace fa

@@ -1,0 +1,264 @@
+// bf16 prefill forward of exact attention on gfx950 matrix cores.
+//
+// Method: the tiled forward with online softmax of the "FlashAttention"
+// concept note, section "是什么" -- a block of query rows stays on chip, K/V
+// blocks stream past it, and a per-row running max m and sum l rescale the
+// partial output so the final O equals softmax(scale Q K^T) V.  Masks and the
+// GQA head mapping are applied inside the tile, as the same section says;
+// tiles that lie wholly above the causal diagonal or beyond a sequence's
+// valid length are never loaded.  The FA2 idea of spreading one head over
+// many work-groups (one per query block) is the grid; the saiita.com.cn
+// explainer, section "二代和三代", credits it for the utilisation gain.
+//
+// Work-group: 4 waves x 32 query rows = 128 rows.  Each KV tile holds 64
+// keys.  Everything per query row lives in one lane pair (lanes i and i+32):
+//   S^T = K Q^T      A = K rows from LDS, B = Q^T kept in VGPRs
+//   O^T += V^T P^T   A = V^T via ds_read_b64_tr_b16, B = P^T straight from
+//                    the S^T accumulators (rounded to bf16)
+// so the row max/sum need one cross-half exchange and the rescale of O by
+// alpha = 2^(m_old - m_new) is lane-local.  Exponentials run in base 2 with
+// scale*log2(e) folded into one FMA.
+#include "fa_device.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+template <int D>
+struct FwdTile {
+  static constexpr int BM = 128;               // query rows per work-group
+  static constexpr int BN = 64;                // keys per KV tile
+  static constexpr int THREADS = 256;          // 4 waves
+  static constexpr int KSTRIDE = D + 8;        // LDS row pitch of K (elements)
+  static constexpr int VSTRIDE = D + 32;       // LDS row pitch of V (elements)
+  static constexpr int DCH = D / 8;            // 16-byte chunks per row
+  static constexpr int CHUNKS = BN * DCH / THREADS;  // chunks per thread per tile
+  static_assert(BN * DCH % THREADS == 0, "tile must split evenly over threads");
+};
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  const int32_t* kv_seqlens;
+  int B, Hq, Hkv, Nq, Nk;
+  int n_qtiles;
+  float scale_log2;  // scale * log2(e)
+};
+
+template <int D, bool CAUSAL, bool PADDED>
+__global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
+  using T = FwdTile<D>;
+  constexpr int BM = T::BM, BN = T::BN;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * T::KSTRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[BN * T::VSTRIDE];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 31, hi = lane >> 5;
+
+  // Work-group -> (query tile, head, batch).  The last (heaviest, under a
+  // causal mask) query tiles of every head are dispatched first.
+  const int bh_count = p.B * p.Hq;
+  const int bh = blockIdx.x % bh_count;
+  const int qt = p.n_qtiles - 1 - (int)(blockIdx.x / bh_count);
+  const int b = bh / p.Hq, hq = bh - b * p.Hq;
+  const int hk = hq / (p.Hq / p.Hkv);
+
+  const int kv_len = PADDED ? clamp_len(p.kv_seqlens, b, p.Nk) : p.Nk;
+  const int q0 = qt * BM;
+  const int diag = p.Nk - p.Nq;  // key j visible to row i iff j <= i + diag
+  int kend = kv_len;
+  if (CAUSAL) {
+    const int q_last = min(q0 + BM, p.Nq) - 1;
+    kend = min(kend, q_last + diag + 1);
+  }
+  const int n_kt = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+  const size_t q_base = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
+  const size_t kv_base = ((size_t)b * p.Hkv + hk) * (size_t)p.Nk;
+
+  // Q^T fragment: lane (li, hi) holds row q0 + 32*wave + li, columns
+  // 16*s + 8*hi .. +7 for each k-step s.
+  const int qrow = q0 + wave * 32 + li;
+  bf16x8 qf[D / 16];
+  if (qrow < p.Nq) {
+    const uint16_t* qp = p.q + (q_base + qrow) * D + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qf[s] = *(const bf16x8*)(qp + 16 * s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qf[s] = bf16x8{};
+  }
+
+  float m = kNegInf;  // running max of scaled scores, base-2 units
+  float l = 0.f;      // running sum over this lane's half of each tile
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+
+  uint4 kreg[T::CHUNKS], vreg[T::CHUNKS];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int c = 0; c < T::CHUNKS; ++c) {
+      const int idx = tid + c * T::THREADS;
+      const int row = idx / T::DCH, col = idx % T::DCH;
+      const int key = kt * BN + row;
+      if (key < kv_len) {
+        const size_t off = (kv_base + key) * D + col * 8;
+        kreg[c] = *(const uint4*)(p.k + off);
+        vreg[c] = *(const uint4*)(p.v + off);
+      } else {
+        kreg[c] = uint4{0, 0, 0, 0};
+        vreg[c] = uint4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int c = 0; c < T::CHUNKS; ++c) {
+      const int idx = tid + c * T::THREADS;
+      const int row = idx / T::DCH, col = idx % T::DCH;
+      *(uint4*)(k_lds + row * T::KSTRIDE + col * 8) = kreg[c];
+      *(uint4*)(v_lds + row * T::VSTRIDE + col * 8) = vreg[c];
+    }
+  };
+
+  // Per-lane offsets of the transposed V read (see fa_device.hpp).
+  const int tr_row = 4 * hi + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  if (n_kt > 0) load_tile(0);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    __syncthreads();  // every wave is done with the previous tile
+    store_tile();
+    __syncthreads();
+    if (kt + 1 < n_kt) load_tile(kt + 1);  // in flight during this tile's math
+
+    // S^T[key][query] = K Q^T for the 64 keys of the tile, two 32-key blocks.
+    f32x16 s[BN / 32];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      s[kb] = f32x16{};
+      const uint16_t* kp = k_lds + (kb * 32 + li) * T::KSTRIDE + 8 * hi;
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) s[kb] = mfma32x32x16(*(const bf16x8*)(kp + 16 * st), qf[st], s[kb]);
+    }
+
+    // Masks, only on tiles that cross the causal diagonal or the valid length.
+    const int k0 = kt * BN;
+    const bool need_mask = (k0 + BN > kv_len) || (CAUSAL && k0 + BN - 1 > q0 + diag);
+    if (need_mask) {
+      const int lim = CAUSAL ? min(kv_len, qrow + diag + 1) : kv_len;  // keys < lim visible
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key >= lim) s[kb][r] = kNegInf;
+        }
+    }
+
+    // Online softmax update of (m, l, O) for this lane's query row.
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, wave_xor32(mx));
+    const float m_new = fmaxf(m, mx * p.scale_log2);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(__builtin_fmaf(s[kb][r], p.scale_log2, -m_use));
+        s[kb][r] = e;
+        rs += e;
+      }
+    l = l * alpha + rs;
+    m = m_new;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+
+    // P^T fragments: registers 8*mm .. 8*mm+7 of key block kb.
+    bf16x8 pf[BN / 16];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        float t[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = s[kb][8 * mm + e];
+        pf[kb * 2 + mm] = pack_bf16x8(t);
+      }
+
+    // O^T[d][query] += V^T P^T.  Element t of either operand pairs with key
+    // kb*32 + 16*mm + 8*(t/4) + 4*hi + t%4.
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          const uint16_t* vp = v_lds + (kb * 32 + 16 * mm + tr_row) * T::VSTRIDE + db * 32 + tr_col;
+          const bf16x8 a = join_bf16x8(lds_read_tr16(vp), lds_read_tr16(vp + 8 * T::VSTRIDE));
+          oacc[db] = mfma32x32x16(a, pf[kb * 2 + mm], oacc[db]);
+        }
+  }
+
+  // Epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l).  Only O and LSE are
+  // ever written to memory.
+  const float lt = l + wave_xor32(l);
+  if (qrow < p.Nq) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* op = p.o + (q_base + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 w;
+        w.x = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+        w.y = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+        *(uint2*)(op + db * 32 + 8 * g + 4 * hi) = w;
+      }
+    if (hi == 0) p.lse[q_base + qrow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+  }
+}
+
+template <int D, bool CAUSAL, bool PADDED>
+static hipError_t launch_fwd_bf16_t(const AttnArgs& a) {
+  using T = FwdTile<D>;
+  FwdParams p;
+  p.q = (const uint16_t*)a.q;
+  p.k = (const uint16_t*)a.k;
+  p.v = (const uint16_t*)a.v;
+  p.o = (uint16_t*)a.o;
+  p.lse = a.lse;
+  p.kv_seqlens = a.kv_seqlens;
+  p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
+  p.n_qtiles = (a.Nq + T::BM - 1) / T::BM;
+  p.scale_log2 = a.scale * kLog2e;
+  const long long grid = (long long)p.n_qtiles * a.B * a.Hq;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PADDED>), dim3((unsigned)grid), dim3(T::THREADS), 0,
+                     a.stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(const AttnArgs& a) {
+  const bool padded = a.kv_seqlens != nullptr;
+  if (a.d == 128) {
+    if (a.causal) return padded ? launch_fwd_bf16_t<128, true, true>(a) : launch_fwd_bf16_t<128, true, false>(a);
+    return padded ? launch_fwd_bf16_t<128, false, true>(a) : launch_fwd_bf16_t<128, false, false>(a);
+  }
+  if (a.causal) return padded ? launch_fwd_bf16_t<64, true, true>(a) : launch_fwd_bf16_t<64, true, false>(a);
+  return padded ? launch_fwd_bf16_t<64, false, true>(a) : launch_fwd_bf16_t<64, false, false>(a);
+}
+
+}  // namespace fa

@@ -1,0 +1,152 @@
+/*
+ * fa.h -- C ABI of the exact tiled attention library (libfa.so, gfx950).
+ *
+ * The operation is exact softmax attention, O = softmax(scale * Q K^T) V, as
+ * defined in the "FlashAttention" concept note (llm-wiki-maxwellmou), section
+ * "是什么": the definition, and the per-block online-softmax update of a
+ * running row max m, row sum l and output O that lets K/V be streamed in
+ * blocks past a Q block held on chip.  The same section places causal masks,
+ * padding masks and multi-head / GQA handling inside the tile, and names
+ * one-token decode as bound by reading the KV cache.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates or frees device memory.
+ *  - Layouts are contiguous, row-major "BHSD":
+ *        q, o : [B, Hq,  Nq, d]      k, v : [B, Hkv, Nk, d]
+ *        lse  : [B, Hq,  Nq] float32 (natural log)
+ *  - dtype (enum fa_dtype) applies to q, k, v and o.  lse and the split-KV
+ *    partials are always float32.  FA_BF16 runs both contractions on bf16
+ *    matrix cores with float32 accumulation (P is rounded to bf16 before the
+ *    P.V product, O is rounded to bf16 at the end); FA_F32 computes in float32
+ *    throughout.
+ *  - d must be 64 or 128.  Hq must be a multiple of Hkv; query head h reads KV
+ *    head h / (Hq / Hkv).
+ *  - scale must be finite and > 0 (the pages use 1/sqrt(d)).
+ *  - Causal masking is aligned bottom-right: key j is visible to query i iff
+ *    j <= i + (Nk - Nq).  With Nq == Nk this is the usual j <= i.
+ *  - kv_seqlens is NULL (all Nk keys valid) or a DEVICE int32[B]: keys
+ *    j >= kv_seqlens[b] of sequence b are excluded.  Values are clamped to
+ *    [0, Nk] on the device (they cannot be checked without a sync).  Key and
+ *    value rows at or beyond a sequence's length are never read.
+ *  - A query row with no visible key gets O = 0 and LSE = -inf.
+ *  - q, k, v, o and the partials must be 16-byte aligned; lse 4-byte aligned.
+ *  - stream is a hipStream_t (NULL = the null stream).  Calls enqueue work and
+ *    return without synchronising.  Arguments are validated on the host before
+ *    any HIP call; a device fault surfaces at the caller's next sync.
+ *  - Every call returns an fa_status; on failure fa_last_error() gives a
+ *    thread-local message.
+ *  - Sizes may be zero: a call with no output elements returns FA_OK without
+ *    launching anything; Nk == 0 (or every length 0) yields O = 0, LSE = -inf.
+ *    Pointers of empty tensors may be NULL.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null / misaligned pointer, negative size, bad scale */
+  FA_ERR_UNSUPPORTED = -2, /* d, dtype, head ratio or num_splits outside the supported set */
+  FA_ERR_WORKSPACE = -3,   /* decode workspace missing or smaller than fa_decode_workspace_bytes */
+  FA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+};
+
+enum fa_dtype { FA_F32 = 0, FA_BF16 = 1 };
+
+/* Split-KV decode partitions each sequence's keys [0, L) into num_splits
+ * chunks of C = ceil(L / num_splits) keys, C rounded up to a multiple of
+ * FA_DECODE_SPLIT_ALIGN; split s covers [s*C, min((s+1)*C, L)) and may be
+ * empty (then its partial is O_s = 0, lse_s = -inf). */
+#define FA_DECODE_SPLIT_ALIGN 128
+#define FA_MAX_SPLITS 256
+
+/*
+ * fa_fwd -- exact attention forward (prefill).
+ *
+ * Implements the definition and the blocked online-softmax update of the
+ * concept note, section "是什么": each work-group holds a block of query rows
+ * on chip, streams the K/V blocks it may see through LDS, and writes only O
+ * and LSE to memory (no score or probability matrix reaches HBM).
+ *
+ *   q   [B,Hq,Nq,d]  in     k, v [B,Hkv,Nk,d] in     o [B,Hq,Nq,d] out
+ *   lse [B,Hq,Nq] float32 out: ln sum_j exp(scale * q_i . k_j) over visible j
+ *   causal: 0 or 1.   kv_seqlens: NULL or device int32[B] (padding mask).
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+           const int32_t* kv_seqlens, int dtype, void* stream);
+
+/*
+ * fa_decode_workspace_bytes -- bytes of device workspace fa_decode needs:
+ * float32 partial outputs [B,Hq,num_splits,d] followed (at a 256-byte aligned
+ * offset) by float32 partial LSEs [B,Hq,num_splits].  Returns 0 for invalid
+ * sizes.
+ */
+size_t fa_decode_workspace_bytes(int B, int Hq, int d, int num_splits);
+
+/*
+ * fa_decode_splitkv -- split-KV single-token decode, first stage.
+ *
+ * The concept note ("是什么", last remarks) notes that one-token decode is
+ * bound by reading the KV cache; here the cache of each sequence is split
+ * into num_splits key ranges (see FA_DECODE_SPLIT_ALIGN) processed by
+ * separate work-groups, and the Hq/Hkv query heads that share a KV head are
+ * processed together so each cache byte is read once.
+ *
+ *   q        [B,Hq,1,d]    in       k_cache, v_cache [B,Hkv,Nk,d] in
+ *   o_part   [B,Hq,S,d]    float32 out: normalised partial output of split s
+ *   lse_part [B,Hq,S]      float32 out: log-sum-exp of split s (-inf if empty)
+ *   num_splits S in [1, FA_MAX_SPLITS].  No causal mask: the single query is
+ *   the newest token and sees every valid key.
+ */
+int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                      float* o_part, float* lse_part,
+                      int B, int Hq, int Hkv, int Nk, int d, float scale,
+                      const int32_t* kv_seqlens, int num_splits, int dtype, void* stream);
+
+/*
+ * fa_lse_merge -- exact merge of split partials (decode second stage).
+ *
+ * The online-softmax update of the concept note ("是什么") applied with the
+ * blocks taken to be the splits: per row, M = max_s lse_s,
+ * LSE = M + ln sum_s exp(lse_s - M), O = sum_s exp(lse_s - LSE) O_s.
+ * Rows whose splits are all empty get O = 0, LSE = -inf.
+ *
+ *   o_part [rows,S,d] float32 in    lse_part [rows,S] float32 in
+ *   o [rows,d] (dtype) out          lse [rows] float32 out
+ */
+int fa_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
+                 int rows, int d, int num_splits, int dtype, void* stream);
+
+/*
+ * fa_decode -- fa_decode_splitkv followed by fa_lse_merge on the same stream,
+ * using a caller-provided device workspace of at least
+ * fa_decode_workspace_bytes(B, Hq, d, num_splits) bytes (256-byte aligned).
+ *   o [B,Hq,1,d] (dtype) out, lse [B,Hq,1] float32 out.
+ */
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+              int B, int Hq, int Hkv, int Nk, int d, float scale, const int32_t* kv_seqlens,
+              int num_splits, void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/* Static string for a status code. */
+const char* fa_status_string(int status);
+
+/* Thread-local detail for the last non-OK return on this thread ("" if none). */
+const char* fa_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

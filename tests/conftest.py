@@ -25,3 +25,11 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU case on stdout (flushed) before it touches the device."""
+    if "gpu" in request.node.keywords:
+        print(f"\n[gpu-case] {request.node.nodeid}", flush=True)
+    yield

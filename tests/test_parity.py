@@ -1,0 +1,111 @@
+"""GPU path vs the fp64 oracle on the five workloads (element by element at
+sizes the oracle finishes in seconds; on sampled rows at full size)."""
+import numpy as np
+import pytest
+import torch
+
+import exact_tiled_attention_08_amd as fa
+from exact_tiled_attention_08_amd import inputs
+import oracle
+
+from fa_testutil import check_fwd, compare, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_cfg1_tiny_fp32_full():
+    q, k, v, _ = inputs.make_inputs(1)
+    assert q.dtype == torch.float32 and q.shape == (1, 1, 128, 64)
+    check_fwd(q, k, v, causal=False, what="cfg1")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_cfg2_bf16_full(causal):
+    q, k, v, _ = inputs.make_inputs(2)
+    assert q.shape == (2, 16, 2048, 64)
+    check_fwd(q, k, v, causal=causal, what=f"cfg2 causal={causal}")
+
+
+def test_cfg3_reduced_full_compare():
+    # same seeds and distribution, fewer heads and a ragged length
+    q, k, v, _ = inputs.make_inputs(3, Hq=2, Hkv=2, Nq=1000, Nk=1000)
+    check_fwd(q, k, v, causal=True, what="cfg3 reduced")
+
+
+def _sample_rows(n, extra=()):
+    base = {0, 1, 2, 63, 64, 127, 128, 129, 255, 256, n // 2, n - 129, n - 128, n - 65, n - 2, n - 1}
+    rng = np.random.default_rng(3)
+    base.update(int(x) for x in rng.integers(0, n, 24))
+    base.update(extra)
+    return np.array(sorted(r for r in base if 0 <= r < n))
+
+
+@pytest.mark.slow
+def test_cfg3_full_size_sampled_rows():
+    q, k, v, _ = inputs.make_inputs(3)
+    assert q.shape == (1, 32, 8192, 128)
+    heads = [(0, h) for h in (0, 7, 13, 31)]
+    check_fwd(q, k, v, causal=True, rows=_sample_rows(8192), heads=heads, what="cfg3 full sampled")
+
+
+def test_cfg4_reduced_full_compare():
+    q, k, v, lens = inputs.make_inputs(4, Hq=8, Hkv=2, Nq=700, Nk=700, len_lo=300, len_hi=700)
+    check_fwd(q, k, v, causal=True, lens=lens, what="cfg4 reduced")
+
+
+@pytest.mark.slow
+def test_cfg4_full_size_sampled_rows():
+    q, k, v, lens = inputs.make_inputs(4)
+    assert q.shape == (4, 32, 4096, 128) and k.shape == (4, 8, 4096, 128)
+    L = lens.tolist()
+    extra = [x + dx for x in L for dx in (-1, 0, 1)]
+    heads = [(b, h) for b in range(4) for h in (0, 5, 30)]
+    check_fwd(q, k, v, causal=True, lens=lens, rows=_sample_rows(4096, extra), heads=heads,
+              what="cfg4 full sampled")
+
+
+def _decode_check(q, k, v, lens, S, sample_pairs=None, what="decode"):
+    qd, kd, vd, ld = to_dev(q, k, v, lens)
+    log(f"  fa_decode q{tuple(q.shape)} cache{tuple(k.shape)} S={S}")
+    o, lse = fa.fa_decode(qd, kd, vd, kv_seqlens=ld, num_splits=S)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    B, Hq = q.shape[:2]
+    g = Hq // k.shape[1]
+    if sample_pairs is None:
+        O_ref, L_ref = oracle.attention_ref(q, k, v, kv_seqlens=lens)
+    else:
+        heads = [(b, hk * g + t) for b, hk in sample_pairs for t in range(g)]
+        O_ref, L_ref = oracle.attention_ref(q, k, v, kv_seqlens=lens, heads=heads)
+    return compare(o, lse, O_ref, L_ref, q.dtype, what)
+
+
+def test_cfg5_reduced_full_compare():
+    q, k, v, _ = inputs.make_inputs(5, B=4, Nk=5000)
+    _decode_check(q, k, v, None, 16, what="cfg5 reduced")
+
+
+@pytest.mark.slow
+def test_cfg5_full_size_sampled():
+    q, k, v, _ = inputs.make_inputs(5)
+    assert q.shape == (64, 32, 1, 128) and k.shape == (64, 8, 32768, 128)
+    pairs = [(b, hk) for b in (0, 1, 31, 63) for hk in (0, 3, 7)]
+    _decode_check(q, k, v, None, 16, sample_pairs=pairs, what="cfg5 full sampled")
+
+
+def test_cfg5_partials_match_oracle_partials():
+    q, k, v, _ = inputs.make_inputs(5, B=2, Hq=8, Hkv=2, Nk=3000)
+    lens = torch.tensor([3000, 1234], dtype=torch.int32)
+    qd, kd, vd, ld = to_dev(q, k, v, lens)
+    S = 16
+    op, lp = fa.fa_decode_splitkv(qd, kd, vd, num_splits=S, kv_seqlens=ld)
+    torch.cuda.synchronize()
+    Op, Lp = oracle.decode_partials_ref(q, k, v, lens, oracle.attention.default_scale(128), S,
+                                        fa.FA_DECODE_SPLIT_ALIGN)
+    compare(op.cpu(), lp.cpu(), Op, Lp, torch.bfloat16, "cfg5 partials")
+    # the merge kernel on the oracle's own partials equals the oracle's merge
+    om, lm = fa.fa_lse_merge(torch.from_numpy(Op).float().cuda(), torch.from_numpy(Lp).float().cuda(),
+                             dtype=torch.float32)
+    torch.cuda.synchronize()
+    Om, Lm = oracle.merge_partials(Op.astype(np.float32), Lp.astype(np.float32))
+    compare(om.cpu()[:, :, 0], lm.cpu()[:, :, 0], Om, Lm, torch.float32, "merge of oracle partials")
