@@ -1,0 +1,222 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * prefill forward, B=1, H=32, N=8192, d=128, causal, bf16 (fa_fwd), and
+  * split-KV decode, B=64, Hq=32, Hkv=8, Nk=32768, d=128, 16 splits, bf16
+    (fa_decode_splitkv + fa_lse_merge).
+Inputs are generated once (seeded), uploaded, and stay resident in HBM.
+
+Prints ONE JSON line.  `value` is the prefill throughput in TFLOP/s, counting
+4*d FLOP per allowed (query, key) pair (2*d for Q.K, 2*d for P.V); the decode
+bandwidth and every kernel's own roofline sit beside it.  Kernel durations
+come from HIP events recorded on the stream the kernels run on.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (N=8K causal d=128); decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU (published 2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0      # HBM3E, 8 TB/s
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
+KERNEL_SOURCES = ["fwd_bf16.hip", "decode_bf16.hip", "fa_device.hpp"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_tiled_attention_08_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_flops(B, H, Nq, Nk, d, causal):
+    """4*d FLOP per allowed (query, key) pair."""
+    if causal:
+        pairs = sum(min(Nk, i + (Nk - Nq) + 1) for i in range(Nq)) if Nq != Nk else Nq * (Nq + 1) // 2
+    else:
+        pairs = Nq * Nk
+    return 4.0 * d * B * H * pairs
+
+
+def decode_bytes(B, Hq, Hkv, Nk, d, elem=2):
+    """Algorithmic HBM bytes: K and V read once, Q read, O and LSE written."""
+    return 2 * B * Hkv * Nk * d * elem + B * Hq * d * elem * 2 + B * Hq * 4
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(n_heads):
+    """Time the fp64 oracle on a bounded sample of the prefill workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from exact_tiled_attention_08_amd import inputs
+    import oracle
+
+    q, k, v, _ = inputs.make_inputs(3)
+    q64, k64, v64 = (x[:, :n_heads].to(dtype=__import__("torch").float64).numpy() for x in (q, k, v))
+    t0 = time.perf_counter()
+    oracle.attention_ref(q64, k64, v64, causal=True)
+    dt = time.perf_counter() - t0
+    flops = prefill_flops(1, n_heads, 8192, 8192, 128, True)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"prefill N=8192 causal d=128, {n_heads} of 32 heads (B=1), fp64 numpy; "
+                      f"{dt:.1f} s; exp runs single-threaded",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-heads", type=int, default=32, help="heads in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path would shard heads or batch across GPUs with no exchange).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_tiled_attention_08_amd as fa
+    from exact_tiled_attention_08_amd import inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    print(f"[bench] device {props.name} CUs={props.multi_processor_count}", file=sys.stderr, flush=True)
+
+    # ---- inputs (seeded, generated on the host once, resident in HBM)
+    c3 = inputs.CONFIGS[3]
+    q3, k3, v3, _ = (t.to(dev) if t is not None else None for t in inputs.make_inputs(3))
+    o3 = torch.empty_like(q3)
+    l3 = torch.empty(q3.shape[:3], dtype=torch.float32, device=dev)
+    c5 = inputs.CONFIGS[5]
+    print("[bench] generating decode cache (2 x 4 GiB)", file=sys.stderr, flush=True)
+    q5, k5, v5, _ = inputs.make_inputs(5)
+    q5, k5, v5 = q5.to(dev), k5.to(dev), v5.to(dev)
+    S = c5["num_splits"]
+    B5, Hq5, Hkv5, Nk5, d5 = c5["B"], c5["Hq"], c5["Hkv"], c5["Nk"], c5["d"]
+    op = torch.empty((B5, Hq5, S, d5), dtype=torch.float32, device=dev)
+    lp = torch.empty((B5, Hq5, S), dtype=torch.float32, device=dev)
+    o5 = torch.empty_like(q5)
+    l5 = torch.empty((B5, Hq5, 1), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fa_fwd(q3, k3, v3, causal=True, out=o3, lse=l3)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.fa_decode_splitkv(q5, k5, v5, num_splits=S, o_part=op, lse_part=lp)
+        if ev is not None:
+            ev[2].record(stream)
+        fa.fa_lse_merge(op, lp, dtype=torch.bfloat16, out=o5, lse=l5)
+        if ev is not None:
+            ev[3].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
+    split_ms = [e[1].elapsed_time(e[2]) for e in events]
+    merge_ms = [e[2].elapsed_time(e[3]) for e in events]
+    avg = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    f_fwd = prefill_flops(c3["B"], c3["Hq"], c3["Nq"], c3["Nk"], c3["d"], True)
+    fwd_tflops = f_fwd / (avg(fwd_ms) * 1e-3) / 1e12
+    dbytes = decode_bytes(B5, Hq5, Hkv5, Nk5, d5)
+    dec_ms = avg(split_ms) + avg(merge_ms)
+    dec_gbs = dbytes / (dec_ms * 1e-3) / 1e9
+    split_gbs = (dbytes - B5 * Hq5 * d5 * 2 - B5 * Hq5 * 4) / (avg(split_ms) * 1e-3) / 1e9
+
+    traffic = load_traffic("fwd_bf16_kernel")
+    rec = {
+        "metric": METRIC,
+        "value": round(fwd_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs; no dataset)",
+        "config": {
+            "workload": "prefill fwd B=1 H=32 N=8192 d=128 causal bf16 + split-KV decode B=64 Hq=32 Hkv=8 "
+                        "Nk=32768 d=128 S=16 bf16",
+            "prefill": {"B": 1, "H": 32, "N": 8192, "d": 128, "causal": True, "mult": c3["mult"]},
+            "decode": {"B": B5, "Hq": Hq5, "Hkv": Hkv5, "Nk": Nk5, "d": d5, "num_splits": S},
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "fwd_bf16_kernel<128,causal>",
+            "achieved": round(fwd_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "flop_per_launch": f_fwd,
+            "avg_launch_ms": round(avg(fwd_ms), 5),
+        },
+        "decode": {
+            "value": round(dec_gbs, 1),
+            "unit": "GB/s",
+            "frac_of_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": dbytes,
+            "avg_split_ms": round(avg(split_ms), 5),
+            "avg_merge_ms": round(avg(merge_ms), 5),
+            "split_kernel_gbs": round(split_gbs, 1),
+            "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                         "traffic": load_traffic("decode_splitkv_bf16_kernel")},
+        },
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] timing the oracle on {args.cpu_heads} heads", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(args.cpu_heads)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
