@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void decode_splitkv_bf16_kernel(DecParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t stage[T::STAGE_ELEMS];
   uint16_t* k_lds = stage;
   uint16_t* v_lds = stage + BN * T::KSTRIDE;
-  static_assert(4 * 32 * (D + 2) * 4 <= T::STAGE_ELEMS * 2, "combine buffer must fit");
+  static_assert(4 * 32 * (D + 3) * 4 <= T::STAGE_ELEMS * 2, "combine buffer must fit");
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void decode_splitkv_bf16_kernel(DecParams p) {
     for (int s = 0; s < D / 16; ++s) qf[s] = bf16x8{};
   }
 
-  float m = kNegInf, l = 0.f;
+  float m = kNegInf, l = 0.f, lr = 0.f;  // max, weight sum, rounded-weight sum
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
@@ -148,11 +148,11 @@ __global__ __launch_bounds__(256) void decode_splitkv_bf16_kernel(DecParams p) {
     float rs = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float e = fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -m_use));
-      s[r] = e;
-      rs += e;
+      s[r] = fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -m_use));
+      rs += s[r];
     }
     l = l * alpha + rs;
+    lr *= alpha;
     m = m_new;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void decode_splitkv_bf16_kernel(DecParams p) {
       float tmp[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) tmp[e] = s[8 * mm + e];
-      pf[mm] = pack_bf16x8(tmp);
+      pf[mm] = pack_bf16x8_sum(tmp, lr);
     }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -180,9 +180,10 @@ __global__ __launch_bounds__(256) void decode_splitkv_bf16_kernel(DecParams p) {
   // Combine the 4 waves' states (disjoint key sets) exactly, then write the
   // split's normalised partial.
   __syncthreads();
-  float* red = (float*)stage;                 // [4 waves][32 cols][D + 2]
-  constexpr int RS = D + 2;
+  float* red = (float*)stage;                 // [4 waves][32 cols][D + 3]
+  constexpr int RS = D + 3;
   const float lt = l + wave_xor32(l);
+  const float lrt = lr + wave_xor32(lr);
   float* my = red + (wave * 32 + li) * RS;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -191,6 +192,7 @@ __global__ __launch_bounds__(256) void decode_splitkv_bf16_kernel(DecParams p) {
   if (hi == 0) {
     my[D] = m;
     my[D + 1] = lt;
+    my[D + 2] = lrt;
   }
   __syncthreads();
   for (int e = tid; e < ncols * D; e += T::THREADS) {
@@ -199,16 +201,17 @@ __global__ __launch_bounds__(256) void decode_splitkv_bf16_kernel(DecParams p) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, red[(w * 32 + col) * RS + D]);
     const float M_use = (M == kNegInf) ? 0.f : M;
-    float acc = 0.f, tot = 0.f;
+    float acc = 0.f, tot = 0.f, totr = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float* rw = red + (w * 32 + col) * RS;
       const float sc = fast_exp2(rw[D] - M_use);
       acc += sc * rw[dd];
       tot += sc * rw[D + 1];
+      totr += sc * rw[D + 2];
     }
     const size_t row = ((size_t)b * p.Hq + hq0 + col) * p.S + split;
-    p.o_part[row * D + dd] = tot > 0.f ? acc / tot : 0.f;
+    p.o_part[row * D + dd] = tot > 0.f ? acc / totr : 0.f;
     if (dd == 0) p.lse_part[row] = tot > 0.f ? (M + __log2f(tot)) * kLn2 : kNegInf;
   }
 }

@@ -30,6 +30,10 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
 constexpr float kNegInf = -__builtin_inff();
+// Lazy-rescale slack of the online softmax, in base-2 exponent units: the
+// reference max is only raised when a new score exceeds it by more than this,
+// so unnormalised probabilities stay <= 2^8.
+constexpr float kRescaleSlack = 8.0f;
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -52,6 +56,21 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
   u.z = pack_bf16x2(x[4], x[5]);
   u.w = pack_bf16x2(x[6], x[7]);
   return __builtin_bit_cast(bf16x8, u);
+}
+
+// Round eight floats to bf16 and add the ROUNDED values to `sum` (one
+// v_dot2_f32_bf16 against (1, 1) per pair).  Summing exactly the weights the
+// P.V product uses makes O a properly normalised average of V rows even
+// though P is rounded: the rounding of a dominant weight cancels in O / l.
+__device__ __forceinline__ bf16x8 pack_bf16x8_sum(const float* x, float& sum) {
+  const bf16x8 p = pack_bf16x8(x);
+  const uint4 u = __builtin_bit_cast(uint4, p);
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.x), ones, sum, false);
+  sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.y), ones, sum, false);
+  sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.z), ones, sum, false);
+  sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.w), ones, sum, false);
+  return p;
 }
 
 // Transposed 4 x 16 read of a row-major bf16 tile in LDS (see header note).

@@ -48,7 +48,7 @@ struct FwdParams {
 };
 
 template <int D, bool CAUSAL, bool PADDED>
-__global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdParams p) {
   using T = FwdTile<D>;
   constexpr int BM = T::BM, BN = T::BN;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * T::KSTRIDE];
@@ -92,8 +92,9 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
     for (int s = 0; s < D / 16; ++s) qf[s] = bf16x8{};
   }
 
-  float m = kNegInf;  // running max of scaled scores, base-2 units
-  float l = 0.f;      // running sum over this lane's half of each tile
+  float m = kNegInf;  // reference (running) max of scaled scores, base-2 units
+  float l = 0.f;      // sum of the weights over this lane's half of each tile
+  float lr = 0.f;     // the same sum over the bf16-rounded weights P.V uses
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
@@ -160,33 +161,42 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
         }
     }
 
-    // Online softmax update of (m, l, O) for this lane's query row.
+    // Online softmax update of (m, l, O) for this lane's query row.  The
+    // reference max m only moves when the tile max exceeds it by more than
+    // kRescaleSlack (base-2 units): every exponent stays <= kRescaleSlack, the
+    // result is unchanged (l and O share the same reference), and the O
+    // rescale -- the costliest VALU step -- is skipped on most tiles.
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, wave_xor32(mx));
-    const float m_new = fmaxf(m, mx * p.scale_log2);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
+    mx = fmaxf(mx, wave_xor32(mx)) * p.scale_log2;
+    if (__any(mx > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - ((m_new == kNegInf) ? 0.f : m_new));
+      m = m_new;
+      l *= alpha;
+      lr *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const float m_use = (m == kNegInf) ? 0.f : m;
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(__builtin_fmaf(s[kb][r], p.scale_log2, -m_use));
-        s[kb][r] = e;
-        rs += e;
+        s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], p.scale_log2, -m_use));
+        rs += s[kb][r];
       }
-    l = l * alpha + rs;
-    m = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    l += rs;
 
-    // P^T fragments: registers 8*mm .. 8*mm+7 of key block kb.
+    // P^T fragments (registers 8*mm .. 8*mm+7 of key block kb), rounded to
+    // bf16; lr accumulates the rounded weights so that O / lr is a properly
+    // normalised average, while the LSE uses the unrounded sum l.
     bf16x8 pf[BN / 16];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
@@ -195,7 +205,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
         float t[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) t[e] = s[kb][8 * mm + e];
-        pf[kb * 2 + mm] = pack_bf16x8(t);
+        pf[kb * 2 + mm] = pack_bf16x8_sum(t, lr);
       }
 
     // O^T[d][query] += V^T P^T.  Element t of either operand pairs with key
@@ -215,8 +225,9 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   // Epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l).  Only O and LSE are
   // ever written to memory.
   const float lt = l + wave_xor32(l);
+  const float lrt = lr + wave_xor32(lr);
   if (qrow < p.Nq) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float inv = lt > 0.f ? 1.f / lrt : 0.f;
     uint16_t* op = p.o + (q_base + qrow) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
