@@ -85,6 +85,31 @@ def cpu_baseline(n_heads):
             "seconds": dt}
 
 
+def profile_only(args, dev):
+    """Run one part of the step args.warmup + args.steps times (for rocprofv3)."""
+    import torch
+
+    import exact_tiled_attention_08_amd as fa
+    from exact_tiled_attention_08_amd import inputs
+
+    if args.only == "copy":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+    elif args.only == "prefill":
+        q, k, v = [t.to(dev) for t in inputs.make_inputs(3)[:3]]
+        for _ in range(args.warmup + args.steps):
+            fa.fa_fwd(q, k, v, causal=True)
+    else:
+        c5 = inputs.CONFIGS[5]
+        q, k, v = [t.to(dev) for t in inputs.make_inputs(5)[:3]]
+        for _ in range(args.warmup + args.steps):
+            fa.fa_decode(q, k, v, num_splits=c5["num_splits"])
+    torch.cuda.synchronize()
+    print(f"[bench] ran {args.only} x{args.warmup + args.steps}", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -92,6 +117,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-heads", type=int, default=32, help="heads in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="profiling aid: run only one part of the step (or a 1 GiB device copy used to "
+                         "calibrate the HBM byte counters) and print no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -107,6 +135,10 @@ def main():
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
     print(f"[bench] device {props.name} CUs={props.multi_processor_count}", file=sys.stderr, flush=True)
+
+    if args.only is not None:
+        profile_only(args, dev)
+        return
 
     # ---- inputs (seeded, generated on the host once, resident in HBM)
     c3 = inputs.CONFIGS[3]

@@ -85,6 +85,27 @@ __device__ __forceinline__ bf16x8 join_bf16x8(i16x4 lo, i16x4 hi) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
+// lane i's 16 bytes land at lds_base + 16*i, lds_base being wave-uniform.
+// Completion is tracked by vmcnt; a __syncthreads() (which waits for vmcnt(0))
+// makes the data visible to the whole work-group.
+__device__ __forceinline__ void load_lds_16B(const void* gptr, void* lds_base) {
+  typedef __attribute__((address_space(1))) void glob_void;
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds((glob_void*)gptr, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// XOR swizzle of the 16-byte chunks of a bf16 K/V tile row in LDS: chunk c of
+// row r lives at position c ^ swz<D>(r).  Chosen so that both the K reads of
+// the S^T product (16 lanes, 16 consecutive rows, one chunk) and the
+// transposed V reads (4 consecutive rows x 4 consecutive chunks per half
+// wave) touch every one of the 64 LDS banks exactly once.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 __device__ __forceinline__ int clamp_len(const int32_t* lens, int b, int nk) {

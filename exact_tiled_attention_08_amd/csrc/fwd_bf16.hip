@@ -18,6 +18,10 @@
 // so the row max/sum need one cross-half exchange and the rescale of O by
 // alpha = 2^(m_old - m_new) is lane-local.  Exponentials run in base 2 with
 // scale*log2(e) folded into one FMA.
+//
+// K/V tiles move HBM -> LDS with direct global_load_lds_dwordx4 copies (no
+// VGPR staging) into two LDS buffers: tile t+1 streams in while tile t is
+// being consumed, with one barrier per tile.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -25,14 +29,14 @@ namespace fa {
 
 template <int D>
 struct FwdTile {
-  static constexpr int BM = 128;               // query rows per work-group
-  static constexpr int BN = 64;                // keys per KV tile
-  static constexpr int THREADS = 256;          // 4 waves
-  static constexpr int KSTRIDE = D + 8;        // LDS row pitch of K (elements)
-  static constexpr int VSTRIDE = D + 32;       // LDS row pitch of V (elements)
-  static constexpr int DCH = D / 8;            // 16-byte chunks per row
-  static constexpr int CHUNKS = BN * DCH / THREADS;  // chunks per thread per tile
-  static_assert(BN * DCH % THREADS == 0, "tile must split evenly over threads");
+  static constexpr int BM = 128;                    // query rows per work-group
+  static constexpr int BN = 64;                     // keys per KV tile
+  static constexpr int THREADS = 256;               // 4 waves
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;              // rows per wave-wide 1 KiB copy
+  static constexpr int TILE = BN * D;               // elements per K (or V) tile
+  static constexpr int COPIES = BN / RPI / 4;       // 1 KiB copies per wave per tile per tensor
+  static_assert(BN % (4 * RPI) == 0, "tile rows must split evenly over the waves");
 };
 
 struct FwdParams {
@@ -51,8 +55,8 @@ template <int D, bool CAUSAL, bool PADDED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdParams p) {
   using T = FwdTile<D>;
   constexpr int BM = T::BM, BN = T::BN;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * T::KSTRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[BN * T::VSTRIDE];
+  // [buffer][K | V][BN rows x D], rows swizzled in 16-byte chunks (swz<D>).
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][T::TILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -78,6 +82,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 
   const size_t q_base = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
   const size_t kv_base = ((size_t)b * p.Hkv + hk) * (size_t)p.Nk;
+  const uint16_t* kg = p.k + kv_base * D;
+  const uint16_t* vg = p.v + kv_base * D;
 
   // Q^T fragment: lane (li, hi) holds row q0 + 32*wave + li, columns
   // 16*s + 8*hi .. +7 for each k-step s.
@@ -99,52 +105,66 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
 
-  uint4 kreg[T::CHUNKS], vreg[T::CHUNKS];
-  auto load_tile = [&](int kt) {
+  // Copy plan: wave w fills rows [w*COPIES*RPI, (w+1)*COPIES*RPI) of each
+  // tile; in copy i, lane l brings row r = (w*COPIES + i)*RPI + l/CPR, source
+  // chunk (l % CPR) ^ swz(r), to LDS position l % CPR of that row.
+  int src_row[T::COPIES], src_col[T::COPIES];
 #pragma unroll
-    for (int c = 0; c < T::CHUNKS; ++c) {
-      const int idx = tid + c * T::THREADS;
-      const int row = idx / T::DCH, col = idx % T::DCH;
-      const int key = kt * BN + row;
-      if (key < kv_len) {
-        const size_t off = (kv_base + key) * D + col * 8;
-        kreg[c] = *(const uint4*)(p.k + off);
-        vreg[c] = *(const uint4*)(p.v + off);
-      } else {
-        kreg[c] = uint4{0, 0, 0, 0};
-        vreg[c] = uint4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&]() {
+  for (int i = 0; i < T::COPIES; ++i) {
+    const int r = (wave * T::COPIES + i) * T::RPI + lane / T::CPR;
+    src_row[i] = r;
+    src_col[i] = ((lane % T::CPR) ^ swz<D>(r)) * 8;
+  }
+  auto issue_tile = [&](int kt, int buf) {
+    const int k0 = kt * BN;
+    const bool tail = k0 + BN > kv_len;  // rows past the length re-read the last valid row
 #pragma unroll
-    for (int c = 0; c < T::CHUNKS; ++c) {
-      const int idx = tid + c * T::THREADS;
-      const int row = idx / T::DCH, col = idx % T::DCH;
-      *(uint4*)(k_lds + row * T::KSTRIDE + col * 8) = kreg[c];
-      *(uint4*)(v_lds + row * T::VSTRIDE + col * 8) = vreg[c];
+    for (int i = 0; i < T::COPIES; ++i) {
+      int row = k0 + src_row[i];
+      if (tail) row = min(row, kv_len - 1);
+      const size_t off = (size_t)row * D + src_col[i];
+      load_lds_16B(kg + off, &lds[buf][0][(wave * T::COPIES + i) * 512]);
+      load_lds_16B(vg + off, &lds[buf][1][(wave * T::COPIES + i) * 512]);
     }
   };
 
-  // Per-lane offsets of the transposed V read (see fa_device.hpp).
-  const int tr_row = 4 * hi + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // Per-lane LDS offsets (elements) of the fragment reads.
+  //  K: row kb*32 + li, chunk 2*st + hi.
+  int k_off[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) k_off[st] = li * D + (((2 * st + hi) ^ swz<D>(li)) * 8);
+  //  V (transposed 4x16 reads): row kb*32 + 16*mm + 8*u + 4*hi + (lane&15)/4,
+  //  column db*32 + 16*((lane>>4)&1) + 4*(lane&3).
+  const int tr_r = 4 * hi + ((lane & 15) >> 2);
+  const int tr_cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // chunk within the 32-column block
+  const int tr_in = 4 * (lane & 1);                               // element within the chunk
+  int v_off[D / 32][2];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = 8 * u + tr_r;
+      v_off[db][u] = r * D + (((4 * db + tr_cc) ^ swz<D>(r)) * 8) + tr_in;
+    }
 
-  if (n_kt > 0) load_tile(0);
+  if (n_kt > 0) issue_tile(0, 0);
   for (int kt = 0; kt < n_kt; ++kt) {
-    __syncthreads();  // every wave is done with the previous tile
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < n_kt) load_tile(kt + 1);  // in flight during this tile's math
+    const int buf = kt & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile kt is in LDS; every wave is done with tile kt-1
+    if (kt + 1 < n_kt) issue_tile(kt + 1, buf ^ 1);
+
+    const uint16_t* kl = lds[buf][0];
+    const uint16_t* vl = lds[buf][1];
 
     // S^T[key][query] = K Q^T for the 64 keys of the tile, two 32-key blocks.
     f32x16 s[BN / 32];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
       s[kb] = f32x16{};
-      const uint16_t* kp = k_lds + (kb * 32 + li) * T::KSTRIDE + 8 * hi;
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st) s[kb] = mfma32x32x16(*(const bf16x8*)(kp + 16 * st), qf[st], s[kb]);
+      for (int st = 0; st < D / 16; ++st)
+        s[kb] = mfma32x32x16(*(const bf16x8*)(kl + kb * 32 * D + k_off[st]), qf[st], s[kb]);
     }
 
     // Masks, only on tiles that cross the causal diagonal or the valid length.
@@ -216,13 +236,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-          const uint16_t* vp = v_lds + (kb * 32 + 16 * mm + tr_row) * T::VSTRIDE + db * 32 + tr_col;
-          const bf16x8 a = join_bf16x8(lds_read_tr16(vp), lds_read_tr16(vp + 8 * T::VSTRIDE));
+          const uint16_t* vp = vl + (kb * 32 + 16 * mm) * D;
+          const bf16x8 a = join_bf16x8(lds_read_tr16(vp + v_off[db][0]), lds_read_tr16(vp + v_off[db][1]));
           oacc[db] = mfma32x32x16(a, pf[kb * 2 + mm], oacc[db]);
         }
   }
 
-  // Epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l).  Only O and LSE are
+  // Epilogue: O = O_acc / lr, LSE = ln2 * (m + log2 l).  Only O and LSE are
   // ever written to memory.
   const float lt = l + wave_xor32(l);
   const float lrt = lr + wave_xor32(lr);
