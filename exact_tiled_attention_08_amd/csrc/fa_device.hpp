@@ -95,6 +95,26 @@ __device__ __forceinline__ void load_lds_16B(const void* gptr, void* lds_base) {
   __builtin_amdgcn_global_load_lds((glob_void*)gptr, (lds_void*)lds_base, 16, 0, 0);
 }
 
+// The same copy issued from inline assembly, so the compiler does not track
+// it as an LDS write: callers order it themselves with s_waitcnt vmcnt and
+// barriers.  gbase and lds_base must be wave-uniform; lane i copies the 16
+// bytes at gbase + voff_bytes into LDS at lds_base + 16*i.  m0 is saved and
+// restored around the copy.  No VGPR is written, so nothing is left in flight
+// towards a register.
+__device__ __forceinline__ void copy16_to_lds(const void* gbase, int voff_bytes, const void* lds_base) {
+  const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_base;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff_bytes), "s"(gbase), "s"(la)
+      : "memory");
+}
+
 // XOR swizzle of the 16-byte chunks of a bf16 K/V tile row in LDS: chunk c of
 // row r lives at position c ^ swz<D>(r).  Chosen so that both the K reads of
 // the S^T product (16 lanes, 16 consecutive rows, one chunk) and the
@@ -106,7 +126,27 @@ __device__ __forceinline__ int swz(int r) {
   else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
+// Swizzle for d = 128 V tiles that are only read transposed: each half wave
+// reads 4 consecutive rows (starting at a multiple of 4) x 4 consecutive
+// chunks, so XOR-ing the chunk with 4*(r % 4) already spreads them over all 64
+// banks, and rows 8 apart share one swizzle (their offset is an immediate).
+__device__ __forceinline__ int swz_v128(int r) { return 4 * (r & 3); }
+
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// max / sum of x over the lane pair (l, l ^ 32) with one v_permlane32_swap:
+// after the swap the two returned registers hold x and the partner's x (in
+// some order) in every lane.
+__device__ __forceinline__ float pair_max32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
 
 __device__ __forceinline__ int clamp_len(const int32_t* lens, int b, int nk) {
   if (lens == nullptr) return nk;

@@ -21,7 +21,10 @@
 //
 // K/V tiles move HBM -> LDS with direct global_load_lds_dwordx4 copies (no
 // VGPR staging) into two LDS buffers: tile t+1 streams in while tile t is
-// being consumed, with one barrier per tile.
+// being consumed, with one barrier per tile.  The two buffers are distinct
+// __shared__ arrays and the tile loop is unrolled by two, so every LDS read
+// names its buffer statically and the compiler can tell the in-flight copies
+// into the other buffer do not alias it (otherwise it waits for them).
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -55,8 +58,12 @@ template <int D, bool CAUSAL, bool PADDED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdParams p) {
   using T = FwdTile<D>;
   constexpr int BM = T::BM, BN = T::BN;
-  // [buffer][K | V][BN rows x D], rows swizzled in 16-byte chunks (swz<D>).
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][T::TILE];
+  // Two buffers of one K and one V tile, BN rows x D, rows swizzled in
+  // 16-byte chunks (swz<D>).
+  __shared__ __attribute__((aligned(1024))) uint16_t k_s0[T::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_s0[T::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_s1[T::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_s1[T::TILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -108,23 +115,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   // Copy plan: wave w fills rows [w*COPIES*RPI, (w+1)*COPIES*RPI) of each
   // tile; in copy i, lane l brings row r = (w*COPIES + i)*RPI + l/CPR, source
   // chunk (l % CPR) ^ swz(r), to LDS position l % CPR of that row.
-  int src_row[T::COPIES], src_col[T::COPIES];
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  int src_row[T::COPIES], src_off[T::COPIES];
 #pragma unroll
   for (int i = 0; i < T::COPIES; ++i) {
     const int r = (wave * T::COPIES + i) * T::RPI + lane / T::CPR;
     src_row[i] = r;
-    src_col[i] = ((lane % T::CPR) ^ swz<D>(r)) * 8;
+    src_off[i] = r * D + ((lane % T::CPR) ^ swz<D>(r)) * 8;
   }
-  auto issue_tile = [&](int kt, int buf) {
+  auto issue_tile = [&](int kt, uint16_t* kdst, uint16_t* vdst) {
     const int k0 = kt * BN;
+    const uint16_t* kt_k = kg + (size_t)k0 * D;
+    const uint16_t* kt_v = vg + (size_t)k0 * D;
     const bool tail = k0 + BN > kv_len;  // rows past the length re-read the last valid row
 #pragma unroll
     for (int i = 0; i < T::COPIES; ++i) {
-      int row = k0 + src_row[i];
-      if (tail) row = min(row, kv_len - 1);
-      const size_t off = (size_t)row * D + src_col[i];
-      load_lds_16B(kg + off, &lds[buf][0][(wave * T::COPIES + i) * 512]);
-      load_lds_16B(vg + off, &lds[buf][1][(wave * T::COPIES + i) * 512]);
+      int off = src_off[i];
+      if (tail) off += (min(k0 + src_row[i], kv_len - 1) - (k0 + src_row[i])) * D;
+      const int dst = (wave_u * T::COPIES + i) * 512;
+      load_lds_16B(kt_k + off, kdst + dst);
+      load_lds_16B(kt_v + off, vdst + dst);
     }
   };
 
@@ -147,24 +157,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
       v_off[db][u] = r * D + (((4 * db + tr_cc) ^ swz<D>(r)) * 8) + tr_in;
     }
 
-  if (n_kt > 0) issue_tile(0, 0);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
+  // One tile: wait for its copies, start the next tile's copies into the
+  // other buffer, then S^T, mask, online softmax and P.V.
+  auto tile_step = [&](int kt, const uint16_t* kl, const uint16_t* vl, uint16_t* kn, uint16_t* vn) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // tile kt is in LDS; every wave is done with tile kt-1
-    if (kt + 1 < n_kt) issue_tile(kt + 1, buf ^ 1);
-
-    const uint16_t* kl = lds[buf][0];
-    const uint16_t* vl = lds[buf][1];
+    if (kt + 1 < n_kt) issue_tile(kt + 1, kn, vn);
 
     // S^T[key][query] = K Q^T for the 64 keys of the tile, two 32-key blocks.
     f32x16 s[BN / 32];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
+      bf16x8 kf[D / 16];
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) kf[st] = *(const bf16x8*)(kl + kb * 32 * D + k_off[st]);
       s[kb] = f32x16{};
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st)
-        s[kb] = mfma32x32x16(*(const bf16x8*)(kl + kb * 32 * D + k_off[st]), qf[st], s[kb]);
+      for (int st = 0; st < D / 16; ++st) s[kb] = mfma32x32x16(kf[st], qf[st], s[kb]);
     }
 
     // Masks, only on tiles that cross the causal diagonal or the valid length.
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, wave_xor32(mx)) * p.scale_log2;
+    mx = pair_max32(mx) * p.scale_log2;
     if (__any(mx > m + kRescaleSlack)) {
       const float m_new = fmaxf(m, mx);
       const float alpha = fast_exp2(m - ((m_new == kNegInf) ? 0.f : m_new));
@@ -240,12 +249,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
           const bf16x8 a = join_bf16x8(lds_read_tr16(vp + v_off[db][0]), lds_read_tr16(vp + v_off[db][1]));
           oacc[db] = mfma32x32x16(a, pf[kb * 2 + mm], oacc[db]);
         }
+  };
+
+  if (n_kt > 0) issue_tile(0, k_s0, v_s0);
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    tile_step(kt, k_s0, v_s0, k_s1, v_s1);
+    if (kt + 1 < n_kt) tile_step(kt + 1, k_s1, v_s1, k_s0, v_s0);
   }
 
   // Epilogue: O = O_acc / lr, LSE = ln2 * (m + log2 l).  Only O and LSE are
   // ever written to memory.
-  const float lt = l + wave_xor32(l);
-  const float lrt = lr + wave_xor32(lr);
+  const float lt = pair_sum32(l);
+  const float lrt = pair_sum32(lr);
   if (qrow < p.Nq) {
     const float inv = lt > 0.f ? 1.f / lrt : 0.f;
     uint16_t* op = p.o + (q_base + qrow) * D;
@@ -260,6 +275,316 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
       }
     if (hi == 0) p.lse[q_base + qrow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
   }
+}
+
+// ---------------------------------------------------------------------------
+// d = 128: eight waves in two groups of four, kept one phase apart ("ping
+// pong").  Waves w and w+4 share a SIMD.  In every phase one group runs its
+// matrix-core work for tile j -- S_j = K_j Q^T and O += V_{j-1} P_{j-1} -- while
+// the other group runs the online-softmax update of its previous tile on the
+// vector ALU, so the two kinds of work overlap on each SIMD instead of
+// alternating inside one wave.  A barrier closes every phase.
+//
+//   phase 2j   : group 0 matrix(j)      group 1 softmax(j-1)
+//   phase 2j+1 : group 0 softmax(j)     group 1 matrix(j)
+//
+// Both groups run the same program -- matrix(j), barrier, softmax(j),
+// barrier -- group 1 simply starting one barrier later.  K/V tiles rotate
+// through three LDS buffers; step j starts copying K_{j+2} and V_{j+1}.
+struct PPTile {
+  static constexpr int D = 128, BM = 256, BN = 64, WAVES = 8, THREADS = 512;
+  static constexpr int TILE = BN * D;                 // elements per K or V tile (16 KiB)
+  static constexpr int CPR = D / 8, RPI = 64 / CPR;   // 16 chunks per row, 4 rows per 1 KiB copy
+  static constexpr int COPIES = BN / RPI / WAVES;     // 1 KiB copies per wave per tile (= 2)
+};
+
+template <bool CAUSAL, bool PADDED>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_pp_kernel(FwdParams p) {
+  using T = PPTile;
+  constexpr int D = T::D, BM = T::BM, BN = T::BN;
+  // buffers 0..2: K tiles, 3..5: V tiles; tile t lives in buffer t % 3.
+  __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[6][T::TILE];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 31, hi = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const bool lead = wave_u < 4;  // group 0 leads, group 1 lags one phase
+
+  const int bh_count = p.B * p.Hq;
+  const int bh = blockIdx.x % bh_count;
+  const int qt = p.n_qtiles - 1 - (int)(blockIdx.x / bh_count);
+  const int b = bh / p.Hq, hq = bh - b * p.Hq;
+  const int hk = hq / (p.Hq / p.Hkv);
+
+  const int kv_len = PADDED ? clamp_len(p.kv_seqlens, b, p.Nk) : p.Nk;
+  const int q0 = qt * BM;
+  const int diag = p.Nk - p.Nq;
+  int kend = kv_len;
+  if (CAUSAL) kend = min(kend, min(q0 + BM, p.Nq) - 1 + diag + 1);
+  const int n_kt = kend > 0 ? (kend + BN - 1) / BN : 0;
+  // tiles this wave's rows can see at all (later tiles are skipped, not masked)
+  const int w_first = q0 + wave_u * 32;
+  int w_kend = kv_len;
+  if (CAUSAL) w_kend = min(w_kend, min(w_first + 32, p.Nq) - 1 + diag + 1);
+  const int w_nkt = w_kend > 0 ? (w_kend + BN - 1) / BN : 0;
+
+  const size_t q_base = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
+  const size_t kv_base = ((size_t)b * p.Hkv + hk) * (size_t)p.Nk;
+  const uint16_t* kg = p.k + kv_base * D;
+  const uint16_t* vg = p.v + kv_base * D;
+
+  const int qrow = w_first + li;
+  bf16x8 qf[D / 16];
+  if (qrow < p.Nq) {
+    const uint16_t* qp = p.q + (q_base + qrow) * D + 8 * hi;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) qf[st] = *(const bf16x8*)(qp + 16 * st);
+  } else {
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) qf[st] = bf16x8{};
+  }
+
+  float m = kNegInf, l = 0.f, lr = 0.f;
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+  f32x16 s[BN / 32];   // S_j, from its matrix phase to its softmax phase
+  bf16x8 pf[BN / 16];  // P_j, from its softmax phase to the next matrix phase
+#pragma unroll
+  for (int kb = 0; kb < BN / 32; ++kb) s[kb] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < BN / 16; ++i) pf[i] = bf16x8{};
+
+  // Copy plan: wave w moves the 1 KiB copies c = 2w, 2w+1 (rows 4c .. 4c+3) of
+  // each K and V tile; lane l brings row 4c + l/16, source chunk
+  // (l % 16) ^ swizzle(row), to LDS position l % 16 (K: swz, V: swz_v128).
+  // Tiles past the last one are clamped to it: the copy then lands in a
+  // buffer no phase reads, which keeps exactly four copies per step.
+  auto copy_tile = [&](const uint16_t* src, int t, uint16_t* dst, bool is_v) {
+    t = min(t, n_kt - 1);
+    const int k0 = t * BN;
+    const uint16_t* base = src + (size_t)k0 * D;
+    const bool tail = k0 + BN > kv_len;  // rows past the length re-read the last valid row
+#pragma unroll
+    for (int i = 0; i < T::COPIES; ++i) {
+      const int r = (wave_u * T::COPIES + i) * T::RPI + (lane >> 4);
+      const int chunk = (lane & 15) ^ (is_v ? swz_v128(r) : swz<D>(r));
+      const int row = tail ? min(k0 + r, kv_len - 1) - k0 : r;
+      copy16_to_lds(base, (row * D + chunk * 8) * 2, dst + (wave_u * T::COPIES + i) * 512);
+    }
+  };
+
+  int k_off[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) k_off[st] = li * D + (((2 * st + hi) ^ swz<D>(li)) * 8);
+  const int tr_r = 4 * hi + ((lane & 15) >> 2);
+  const int tr_cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_in = 4 * (lane & 1);
+  int v_off[D / 32];  // row tr_r; the second read of a pair is 8 rows on
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)  // V region starts at buffer 3
+    v_off[db] = 3 * T::TILE + tr_r * D + (((4 * db + tr_cc) ^ swz_v128(tr_r)) * 8) + tr_in;
+  // All fragment reads address kv_lds[0] + (lane offset register) + (a
+  // compile-time offset below 64 KiB), so each buffer is an instruction
+  // immediate on the same 16 address registers.
+  const uint16_t* lds0 = kv_lds[0];
+
+  // Matrix work of tile j, as a software pipeline over eight groups of four
+  // MFMAs: G0..G3 = K rows (key block g/2, k-steps 4*(g%2) .. +3) for
+  // S_j = K_j Q^T; G4..G7 = V^T columns of d-block g-4 for O += V_{j-1} P_{j-1}.
+  // The fragments of group g+1 are read from LDS while the MFMAs of group g
+  // run; sched_barrier keeps the compiler from hoisting more reads (and
+  // registers) than that.
+  auto load_group = [&](int g, int kbuf, int vbuf, bf16x8* f) {
+    if (g < 4) {
+      const int kb = g >> 1, st0 = 4 * (g & 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = *(const bf16x8*)(lds0 + k_off[st0 + i] + (kbuf * T::TILE + kb * 32 * D));
+    } else {
+      const int db = g - 4;
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          const int c = vbuf * T::TILE + (kb * 32 + 16 * mm) * D;
+          f[kb * 2 + mm] = join_bf16x8(lds_read_tr16(lds0 + v_off[db] + c), lds_read_tr16(lds0 + v_off[db] + c + 8 * D));
+        }
+    }
+  };
+  auto mfma_group = [&](int g, const bf16x8* f) {
+    if (g < 4) {
+      const int kb = g >> 1, st0 = 4 * (g & 1);
+      if (st0 == 0) s[kb] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[kb] = mfma32x32x16(f[i], qf[st0 + i], s[kb]);
+    } else {
+      const int db = g - 4;
+#pragma unroll
+      for (int i = 0; i < BN / 16; ++i) oacc[db] = mfma32x32x16(f[i], pf[i], oacc[db]);
+    }
+  };
+  // Positions 0..3 of the pipeline run the P.V groups (G4..G7) and positions
+  // 4..7 the S groups (G0..G3): P_{j-1} is dead before S_j comes alive.
+  auto run_groups = [&](int i0, int i1, int kbuf, int vbuf) {
+    auto grp = [](int i) { return i < 4 ? i + 4 : i - 4; };
+    bf16x8 fa[4], fb[4];
+    load_group(grp(i0), kbuf, vbuf, fa);
+#pragma unroll
+    for (int i = i0; i < i1; ++i) {
+      if (i + 1 < i1) load_group(grp(i + 1), kbuf, vbuf, ((i - i0) & 1) ? fa : fb);
+      mfma_group(grp(i), ((i - i0) & 1) ? fb : fa);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Every step runs all eight groups -- one code path keeps the register
+  // allocation tight.  Work a wave does not need is harmless: S_j of a tile
+  // past the wave's range is never used, and P.V runs with P = 0 (at j = 0,
+  // and after a skipped softmax) against finite V data.
+  auto matrix_phase = [&](int kbuf, int vbuf) {
+    __builtin_amdgcn_s_setprio(1);
+    run_groups(0, 8, kbuf, vbuf);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Online-softmax update for tile j (S_j -> P_j), as in the 4-wave kernel.
+  auto softmax_phase = [&](int j) {
+    if (j >= w_nkt) {
+#pragma unroll
+      for (int i = 0; i < BN / 16; ++i) pf[i] = bf16x8{};
+      return;
+    }
+    const int k0 = j * BN;
+    const bool need_mask = (k0 + BN > kv_len) || (CAUSAL && k0 + BN - 1 > w_first + diag);
+    if (need_mask) {
+      // key k0 + 4*hi + c(kb, r) is visible iff c < rel
+      const int rel = (CAUSAL ? min(kv_len, qrow + diag + 1) : kv_len) - k0 - 4 * hi;
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) >= rel) s[kb][r] = kNegInf;
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = pair_max32(mx) * p.scale_log2;
+    if (__any(mx > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - ((m_new == kNegInf) ? 0.f : m_new));
+      m = m_new;
+      l *= alpha;
+      lr *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const float m_use = (m == kNegInf) ? 0.f : m;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], p.scale_log2, -m_use));
+        rs += s[kb][r];
+      }
+    l += rs;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        float t[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = s[kb][8 * mm + e];
+        pf[kb * 2 + mm] = pack_bf16x8_sum(t, lr);
+      }
+  };
+
+  // Each step issues exactly four copies per wave (K_{j+2}, V_{j+1}).  A
+  // wave's copies of K_{j+1} and V_j (from step j-1) must be complete before
+  // the barrier that ends global phase 2j+1 -- for group 1 that is its first
+  // barrier of step j.  Every wave waits before both of its barriers, leaving
+  // only the four copies of the current step in flight (vmcnt 4); keeping the
+  // loop body free of group-dependent code stops the compiler from cloning it
+  // per group.  lgkmcnt(0) retires this wave's LDS reads before any barrier, so
+  // a buffer is free once the barrier after its last use has passed.
+  auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  auto wait_copies = [&]() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); };
+
+  // Step 0 multiplies P = 0 by V buffer 2, which no copy has filled yet:
+  // give it finite contents.
+  for (int i = tid; i < T::TILE / 8; i += T::THREADS) ((uint4*)kv_lds[5])[i] = uint4{0, 0, 0, 0};
+  if (n_kt > 0) {
+    copy_tile(kg, 0, kv_lds[0], false);
+    copy_tile(kg, 1, kv_lds[1], false);
+    copy_tile(vg, 0, kv_lds[3], true);
+    wait_copies();  // K_0 is in
+  }
+  barrier();
+  if (!lead) barrier();
+  // Step j: start K_{j+2} (into the buffer of K_{j-1}) and V_{j+1} (into the
+  // buffer of V_{j-2}); matrix work on K_j and V_{j-1}; softmax of S_j.  The
+  // loop is unrolled by three so every buffer is a compile-time offset.
+  auto step = [&](int j, int b0, int b1, int b2) {
+    copy_tile(kg, j + 2, kv_lds[b2], false);
+    copy_tile(vg, j + 1, kv_lds[3 + b1], true);
+    matrix_phase(b0, b2);  // K_j in K buffer b0, V_{j-1} in V buffer b2
+    wait_copies();
+    barrier();
+    softmax_phase(j);
+    wait_copies();
+    barrier();
+  };
+  // A work-group with no visible tile (empty sequence, or every row above
+  // the causal diagonal) runs no step: its copies would address tile -1.
+  if (n_kt > 0) {
+    for (int j = 0; j <= n_kt; j += 3) {
+      step(j, 0, 1, 2);
+      if (j + 1 <= n_kt) step(j + 1, 1, 2, 0);
+      if (j + 2 <= n_kt) step(j + 2, 2, 0, 1);
+    }
+  }
+  if (lead) barrier();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the clamped copies before exit
+
+  const float lt = pair_sum32(l);
+  const float lrt = pair_sum32(lr);
+  if (qrow < p.Nq) {
+    const float inv = lt > 0.f ? 1.f / lrt : 0.f;
+    uint16_t* op = p.o + (q_base + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 w;
+        w.x = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+        w.y = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+        *(uint2*)(op + db * 32 + 8 * g + 4 * hi) = w;
+      }
+    if (hi == 0) p.lse[q_base + qrow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+  }
+}
+
+template <bool CAUSAL, bool PADDED>
+static hipError_t launch_fwd_bf16_pp(const AttnArgs& a) {
+  FwdParams p;
+  p.q = (const uint16_t*)a.q;
+  p.k = (const uint16_t*)a.k;
+  p.v = (const uint16_t*)a.v;
+  p.o = (uint16_t*)a.o;
+  p.lse = a.lse;
+  p.kv_seqlens = a.kv_seqlens;
+  p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
+  p.n_qtiles = (a.Nq + PPTile::BM - 1) / PPTile::BM;
+  p.scale_log2 = a.scale * kLog2e;
+  const long long grid = (long long)p.n_qtiles * a.B * a.Hq;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fwd_bf16_pp_kernel<CAUSAL, PADDED>), dim3((unsigned)grid), dim3(PPTile::THREADS), 0,
+                     a.stream, p);
+  return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, bool PADDED>
@@ -285,8 +610,8 @@ static hipError_t launch_fwd_bf16_t(const AttnArgs& a) {
 hipError_t launch_fwd_bf16(const AttnArgs& a) {
   const bool padded = a.kv_seqlens != nullptr;
   if (a.d == 128) {
-    if (a.causal) return padded ? launch_fwd_bf16_t<128, true, true>(a) : launch_fwd_bf16_t<128, true, false>(a);
-    return padded ? launch_fwd_bf16_t<128, false, true>(a) : launch_fwd_bf16_t<128, false, false>(a);
+    if (a.causal) return padded ? launch_fwd_bf16_pp<true, true>(a) : launch_fwd_bf16_pp<true, false>(a);
+    return padded ? launch_fwd_bf16_pp<false, true>(a) : launch_fwd_bf16_pp<false, false>(a);
   }
   if (a.causal) return padded ? launch_fwd_bf16_t<64, true, true>(a) : launch_fwd_bf16_t<64, true, false>(a);
   return padded ? launch_fwd_bf16_t<64, false, true>(a) : launch_fwd_bf16_t<64, false, false>(a);
