@@ -20,8 +20,11 @@ LIB = os.path.join(PKG, "libfa.so")
 SOURCES = ["fwd_bf16.hip", "decode_bf16.hip", "fwd_f32.hip", "api.cpp"]
 ARCH = "gfx950"
 
-# Packed-FP32 instruction forms are kept out of every kernel.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed-FP32 instruction forms are kept out of every kernel.  LDS addresses
+# in these kernels are never negative, so constant parts of DS addresses may
+# always be folded into the instructions' offset field.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-Xclang", "-target-feature", "-Xclang", "+unsafe-ds-offset-folding"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-command-line-argument"]
 

@@ -385,39 +385,40 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)  // V region starts at buffer 3
     v_off[db] = 3 * T::TILE + tr_r * D + (((4 * db + tr_cc) ^ swz_v128(tr_r)) * 8) + tr_in;
-  // All fragment reads address kv_lds[0] + (lane offset register) + (a
-  // compile-time offset below 64 KiB), so each buffer is an instruction
-  // immediate on the same 16 address registers.
+  // Fragment reads address lds0 + (per-step address register) + (a
+  // compile-time offset): the step adds its buffer's base to the lane offsets
+  // once, so one loop body serves every buffer.  The empty asm hides the lane
+  // offsets' known bits, so the compiler keeps the constant parts as additions
+  // it can fold into the DS instructions' offset field (the library is built
+  // with DS offset folding allowed: these addresses are never negative).
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) asm volatile("" : "+v"(k_off[st]));
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) asm volatile("" : "+v"(v_off[db]));
   const uint16_t* lds0 = kv_lds[0];
-
-  // Matrix work of tile j, as a software pipeline over eight groups of four
-  // MFMAs: G0..G3 = K rows (key block g/2, k-steps 4*(g%2) .. +3) for
-  // S_j = K_j Q^T; G4..G7 = V^T columns of d-block g-4 for O += V_{j-1} P_{j-1}.
-  // The fragments of group g+1 are read from LDS while the MFMAs of group g
-  // run; sched_barrier keeps the compiler from hoisting more reads (and
-  // registers) than that.
-  auto load_group = [&](int g, int kbuf, int vbuf, bf16x8* f) {
+  int ka[D / 16], va[D / 32];  // this step's K / V fragment offsets (elements)
+  auto load_group = [&](int g, bf16x8* f) {
     if (g < 4) {
       const int kb = g >> 1, st0 = 4 * (g & 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f[i] = *(const bf16x8*)(lds0 + k_off[st0 + i] + (kbuf * T::TILE + kb * 32 * D));
+      for (int i = 0; i < 4; ++i) f[i] = *(const bf16x8*)(lds0 + ka[st0 + i] + kb * 32 * D);
     } else {
       const int db = g - 4;
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-          const int c = vbuf * T::TILE + (kb * 32 + 16 * mm) * D;
-          f[kb * 2 + mm] = join_bf16x8(lds_read_tr16(lds0 + v_off[db] + c), lds_read_tr16(lds0 + v_off[db] + c + 8 * D));
+          const int c = (kb * 32 + 16 * mm) * D;
+          f[kb * 2 + mm] = join_bf16x8(lds_read_tr16(lds0 + va[db] + c), lds_read_tr16(lds0 + va[db] + c + 8 * D));
         }
     }
   };
   auto mfma_group = [&](int g, const bf16x8* f) {
     if (g < 4) {
       const int kb = g >> 1, st0 = 4 * (g & 1);
-      if (st0 == 0) s[kb] = f32x16{};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[kb] = mfma32x32x16(f[i], qf[st0 + i], s[kb]);
+      for (int i = 0; i < 4; ++i)
+        s[kb] = mfma32x32x16(f[i], qf[st0 + i], (st0 == 0 && i == 0) ? f32x16{} : s[kb]);
     } else {
       const int db = g - 4;
 #pragma unroll
@@ -426,13 +427,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   // Positions 0..3 of the pipeline run the P.V groups (G4..G7) and positions
   // 4..7 the S groups (G0..G3): P_{j-1} is dead before S_j comes alive.
-  auto run_groups = [&](int i0, int i1, int kbuf, int vbuf) {
+  auto run_groups = [&](int i0, int i1) {
     auto grp = [](int i) { return i < 4 ? i + 4 : i - 4; };
     bf16x8 fa[4], fb[4];
-    load_group(grp(i0), kbuf, vbuf, fa);
+    load_group(grp(i0), fa);
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
-      if (i + 1 < i1) load_group(grp(i + 1), kbuf, vbuf, ((i - i0) & 1) ? fa : fb);
+      if (i + 1 < i1) load_group(grp(i + 1), ((i - i0) & 1) ? fa : fb);
       mfma_group(grp(i), ((i - i0) & 1) ? fb : fa);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -442,9 +443,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // past the wave's range is never used, and P.V runs with P = 0 (at j = 0,
   // and after a skipped softmax) against finite V data.
   auto matrix_phase = [&](int kbuf, int vbuf) {
-    __builtin_amdgcn_s_setprio(1);
-    run_groups(0, 8, kbuf, vbuf);
-    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) ka[st] = k_off[st] + kbuf * T::TILE;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) va[db] = v_off[db] + vbuf * T::TILE;
+    run_groups(0, 8);
   };
 
   // Online-softmax update for tile j (S_j -> P_j), as in the 4-wave kernel.
@@ -465,11 +468,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int r = 0; r < 16; ++r)
           if (kb * 32 + 8 * (r >> 2) + (r & 3) >= rel) s[kb][r] = kNegInf;
     }
-    float mx = kNegInf;
+    // Row max, exponentials and the two row sums, with the reductions split
+    // into four independent partial chains (short dependency chains keep the
+    // vector ALU busy).
+    float mxp[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      for (int r = 0; r < 16; ++r) mxp[r & 3] = fmaxf(mxp[r & 3], s[kb][r]);
+    float mx = fmaxf(fmaxf(mxp[0], mxp[1]), fmaxf(mxp[2], mxp[3]));
     mx = pair_max32(mx) * p.scale_log2;
     if (__any(mx > m + kRescaleSlack)) {
       const float m_new = fmaxf(m, mx);
@@ -483,15 +490,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
     const float m_use = (m == kNegInf) ? 0.f : m;
-    float rs = 0.f;
+    float rsp[4] = {0.f, 0.f, 0.f, 0.f}, lrp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], p.scale_log2, -m_use));
-        rs += s[kb][r];
+        rsp[r & 3] += s[kb][r];
       }
-    l += rs;
+    l += (rsp[0] + rsp[1]) + (rsp[2] + rsp[3]);
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
@@ -499,8 +506,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         float t[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) t[e] = s[kb][8 * mm + e];
-        pf[kb * 2 + mm] = pack_bf16x8_sum(t, lr);
+        pf[kb * 2 + mm] = pack_bf16x8_sum(t, lrp[kb * 2 + mm]);
       }
+    lr += (lrp[0] + lrp[1]) + (lrp[2] + lrp[3]);
   };
 
   // Each step issues exactly four copies per wave (K_{j+2}, V_{j+1}).  A
@@ -526,25 +534,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   barrier();
   if (!lead) barrier();
   // Step j: start K_{j+2} (into the buffer of K_{j-1}) and V_{j+1} (into the
-  // buffer of V_{j-2}); matrix work on K_j and V_{j-1}; softmax of S_j.  The
-  // loop is unrolled by three so every buffer is a compile-time offset.
-  auto step = [&](int j, int b0, int b1, int b2) {
-    copy_tile(kg, j + 2, kv_lds[b2], false);
-    copy_tile(vg, j + 1, kv_lds[3 + b1], true);
-    matrix_phase(b0, b2);  // K_j in K buffer b0, V_{j-1} in V buffer b2
-    wait_copies();
-    barrier();
-    softmax_phase(j);
-    wait_copies();
-    barrier();
-  };
+  // buffer of V_{j-2}); matrix work on K_j and V_{j-1}; softmax of S_j.
   // A work-group with no visible tile (empty sequence, or every row above
   // the causal diagonal) runs no step: its copies would address tile -1.
   if (n_kt > 0) {
-    for (int j = 0; j <= n_kt; j += 3) {
-      step(j, 0, 1, 2);
-      if (j + 1 <= n_kt) step(j + 1, 1, 2, 0);
-      if (j + 2 <= n_kt) step(j + 2, 2, 0, 1);
+    for (int j = 0; j <= n_kt; ++j) {
+      const int b0 = j % 3, b1 = (j + 1) % 3, b2 = (j + 2) % 3;
+      copy_tile(kg, j + 2, kv_lds[b2], false);
+      copy_tile(vg, j + 1, kv_lds[3 + b1], true);
+      matrix_phase(b0, b2);  // K_j in K buffer b0, V_{j-1} in V buffer b2
+      wait_copies();
+      barrier();
+      softmax_phase(j);
+      wait_copies();
+      barrier();
     }
   }
   if (lead) barrier();
