@@ -113,8 +113,8 @@ def profile_only(args, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100, help="untimed steps (about 0.2 s; lets clocks settle)")
     ap.add_argument("--cpu-heads", type=int, default=32, help="heads in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
@@ -197,7 +197,7 @@ def main():
     dec_gbs = dbytes / (dec_ms * 1e-3) / 1e9
     split_gbs = (dbytes - B5 * Hq5 * d5 * 2 - B5 * Hq5 * 4) / (avg(split_ms) * 1e-3) / 1e9
 
-    traffic = load_traffic("fwd_bf16_kernel")
+    traffic = load_traffic("fwd_bf16_pp_kernel")
     rec = {
         "metric": METRIC,
         "value": round(fwd_tflops, 2),
@@ -219,7 +219,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "fwd_bf16_kernel<128,causal>",
+            "kernel": "fwd_bf16_pp_kernel<causal>",
             "achieved": round(fwd_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
@@ -238,7 +238,7 @@ def main():
             "split_kernel_gbs": round(split_gbs, 1),
             "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-                         "traffic": load_traffic("decode_splitkv_bf16_kernel")},
+                         "traffic": load_traffic("decode_splitkv_bf16_kernel+lse_merge_kernel")},
         },
         "kernel_source_hash": kernel_source_hash(),
     }
