@@ -115,6 +115,27 @@ __device__ __forceinline__ void copy16_to_lds(const void* gbase, int voff_bytes,
       : "memory");
 }
 
+// Two such copies under one m0 setting.  Copy 0: lane i reads the 16 bytes
+// at gbase + voff0 and writes them to lds_base + 16*i.  Copy 1: it reads
+// gbase + voff1 + 1024 and writes lds_base + 1024 + 16*i (the instruction
+// offset applies to both the global and the LDS address).  Offsets are
+// unsigned: callers pass a gbase 1 KiB below their data so that both offsets
+// stay non-negative.
+__device__ __forceinline__ void copy16x2_to_lds(const void* gbase, int voff0, int voff1, const void* lds_base) {
+  const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_base;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %3\n\t"
+      "global_load_lds_dwordx4 %2, %3 offset:1024\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff0), "v"(voff1), "s"(gbase), "s"(la)
+      : "memory");
+}
+
 // XOR swizzle of the 16-byte chunks of a bf16 K/V tile row in LDS: chunk c of
 // row r lives at position c ^ swz<D>(r).  Chosen so that both the K reads of
 // the S^T product (16 lanes, 16 consecutive rows, one chunk) and the

@@ -345,6 +345,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int st = 0; st < D / 16; ++st) qf[st] = bf16x8{};
   }
 
+  // Retire the Q loads here.  Their first use is inside the tile loop, and
+  // the compiler's wait for them there would be a vmcnt count that, in every
+  // later step, also waits for that step's K/V copies.
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) asm volatile("" : "+v"(qf[st]));
+
   float m = kNegInf, l = 0.f, lr = 0.f;
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -366,13 +372,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int k0 = t * BN;
     const uint16_t* base = src + (size_t)k0 * D;
     const bool tail = k0 + BN > kv_len;  // rows past the length re-read the last valid row
+    int voff[T::COPIES];
 #pragma unroll
     for (int i = 0; i < T::COPIES; ++i) {
       const int r = (wave_u * T::COPIES + i) * T::RPI + (lane >> 4);
       const int chunk = (lane & 15) ^ (is_v ? swz_v128(r) : swz<D>(r));
       const int row = tail ? min(k0 + r, kv_len - 1) - k0 : r;
-      copy16_to_lds(base, (row * D + chunk * 8) * 2, dst + (wave_u * T::COPIES + i) * 512);
+      voff[i] = (row * D + chunk * 8) * 2;
     }
+    // the wave's two copies are adjacent in LDS: one m0 setting serves both
+    static_assert(T::COPIES == 2, "copies are issued in pairs");
+    copy16x2_to_lds((const char*)base - 1024, voff[0] + 1024, voff[1], dst + wave_u * T::COPIES * 512);
   };
 
   int k_off[D / 16];
@@ -397,32 +407,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int db = 0; db < D / 32; ++db) asm volatile("" : "+v"(v_off[db]));
   const uint16_t* lds0 = kv_lds[0];
   int ka[D / 16], va[D / 32];  // this step's K / V fragment offsets (elements)
+  // Consecutive MFMAs always accumulate into different registers: a chain of
+  // dependent MFMAs on one accumulator issues far below the matrix-core rate,
+  // two or more interleaved chains keep it busy.
+  //   S group g (0..3): k-steps 2g, 2g+1 for both key blocks, alternating
+  //   P.V group 4+i:    key slice i (16 keys) for all four d-blocks
   auto load_group = [&](int g, bf16x8* f) {
     if (g < 4) {
-      const int kb = g >> 1, st0 = 4 * (g & 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f[i] = *(const bf16x8*)(lds0 + ka[st0 + i] + kb * 32 * D);
+      for (int i = 0; i < 4; ++i) f[i] = *(const bf16x8*)(lds0 + ka[2 * g + (i >> 1)] + (i & 1) * 32 * D);
     } else {
-      const int db = g - 4;
+      const int c = (((g - 4) >> 1) * 32 + 16 * ((g - 4) & 1)) * D;
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          const int c = (kb * 32 + 16 * mm) * D;
-          f[kb * 2 + mm] = join_bf16x8(lds_read_tr16(lds0 + va[db] + c), lds_read_tr16(lds0 + va[db] + c + 8 * D));
-        }
+      for (int db = 0; db < D / 32; ++db)
+        f[db] = join_bf16x8(lds_read_tr16(lds0 + va[db] + c), lds_read_tr16(lds0 + va[db] + c + 8 * D));
     }
   };
   auto mfma_group = [&](int g, const bf16x8* f) {
     if (g < 4) {
-      const int kb = g >> 1, st0 = 4 * (g & 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s[kb] = mfma32x32x16(f[i], qf[st0 + i], (st0 == 0 && i == 0) ? f32x16{} : s[kb]);
+      for (int i = 0; i < 4; ++i) {
+        const int kb = i & 1, st = 2 * g + (i >> 1);
+        s[kb] = mfma32x32x16(f[i], qf[st], st == 0 ? f32x16{} : s[kb]);
+      }
     } else {
-      const int db = g - 4;
 #pragma unroll
-      for (int i = 0; i < BN / 16; ++i) oacc[db] = mfma32x32x16(f[i], pf[i], oacc[db]);
+      for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32x32x16(f[db], pf[g - 4], oacc[db]);
     }
   };
   // Positions 0..3 of the pipeline run the P.V groups (G4..G7) and positions
@@ -540,9 +550,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (n_kt > 0) {
     for (int j = 0; j <= n_kt; ++j) {
       const int b0 = j % 3, b1 = (j + 1) % 3, b2 = (j + 2) % 3;
+      matrix_phase(b0, b2);  // K_j in K buffer b0, V_{j-1} in V buffer b2
+      // Copies go out after the matrix work is issued: at the start of the
+      // phase all four waves of the group would queue them at once, holding
+      // back their first MFMAs.
       copy_tile(kg, j + 2, kv_lds[b2], false);
       copy_tile(vg, j + 1, kv_lds[3 + b1], true);
-      matrix_phase(b0, b2);  // K_j in K buffer b0, V_{j-1} in V buffer b2
       wait_copies();
       barrier();
       softmax_phase(j);
