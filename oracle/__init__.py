@@ -13,6 +13,7 @@ forms, invariants, brute force and independent library routines; none is
 from .attention import (  # noqa: F401
     attention_ref,
     attention_probs_ref,
+    attention_bwd_ref,
     online_softmax_blocked,
     merge_partials,
     split_bounds,

@@ -154,6 +154,54 @@ def attention_probs_ref(q, k, v, causal=False, kv_seqlens=None, scale=None):
     return P
 
 
+def attention_bwd_ref(q, k, v, do, causal=False, kv_seqlens=None, scale=None):
+    """Gradients of exact attention, fp64: (dQ, dK, dV) for the loss sum(dO * O).
+
+    The pages say only that the backward pass recomputes the intermediates
+    instead of storing them (Exam deep-dive, section 技術版, "Recomputation";
+    Interview note, section 节省显存，不等于所有内存都变少).  What it computes is
+    the derivative of the forward definition above, written out with S and P
+    materialised, per (batch, query head):
+        dV = P^T dO
+        dP = dO V^T
+        dS = P * (dP - rowsum(dO * O))      (softmax Jacobian, row by row)
+        dQ = scale * dS K
+        dK = scale * dS^T Q
+    Disallowed pairs have P = 0 and so dS = 0.  With GQA every query head adds
+    its dK, dV into the KV head it reads.  A row with no allowed key has O = 0
+    and contributes nothing.
+    q, do: [B, Hq, Nq, d]; k, v: [B, Hkv, Nk, d].  Returns fp64 arrays shaped
+    like q, k and v.
+    """
+    q = to_f64(q); k = to_f64(k); v = to_f64(v); do = to_f64(do)
+    _check_shapes(q, k, v)
+    if do.shape != q.shape:
+        raise ValueError("do must be shaped like q")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = default_scale(d)
+    scale = float(np.float32(scale))
+    if kv_seqlens is not None:
+        kv_seqlens = to_f64(kv_seqlens).astype(np.int64)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        allowed = _allowed(Nq, Nk, _valid_length(kv_seqlens, b, Nk), causal)
+        for hq in range(Hq):
+            hk = _head_map(hq, Hq, Hkv)
+            o, _, P = _one_head(q[b, hq], k[b, hk], v[b, hk], allowed, scale)
+            g = do[b, hq]
+            dv[b, hk] += P.T @ g
+            dP = g @ v[b, hk].T
+            Dr = (g * o).sum(axis=1)
+            dS = P * (dP - Dr[:, None])
+            dq[b, hq] = scale * (dS @ k[b, hk])
+            dk[b, hk] += scale * (dS.T @ q[b, hq])
+    return dq, dk, dv
+
+
 def online_softmax_blocked(qh, kh, vh, block, scale, allowed=None):
     """The per-block online-softmax update of the concept note, section "是什么".
 

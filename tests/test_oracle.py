@@ -204,10 +204,76 @@ def check_split_bounds():
     assert oracle.split_bounds(32768, 16, 128)[1] == (2048, 4096)
 
 
+def _loss_grads_fd(q, k, v, do, causal, lens, scale, h=1e-5):
+    """Central differences of sum(dO * O) through the forward oracle."""
+    def loss(q_, k_, v_):
+        O, _ = oracle.attention_ref(q_, k_, v_, causal=causal, kv_seqlens=lens, scale=scale)
+        return float((do * O).sum())
+    grads = []
+    for which in range(3):
+        args = [q.copy(), k.copy(), v.copy()]
+        g = np.zeros_like(args[which])
+        for idx in np.ndindex(*g.shape):
+            a_p = [x.copy() for x in args]; a_m = [x.copy() for x in args]
+            a_p[which][idx] += h; a_m[which][idx] -= h
+            g[idx] = (loss(*a_p) - loss(*a_m)) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+def check_bwd_finite_differences():
+    # brute force: every input element perturbed, GQA (2 query heads per KV
+    # head), causal with Nq != Nk, and a padded batch entry
+    q, k, v = rand(2, 2, 4, 3), rand(2, 1, 5, 3), rand(2, 1, 5, 3)
+    do = rand(2, 2, 4, 3)
+    for causal, lens in ((True, None), (False, np.array([5, 3])), (True, np.array([2, 5]))):
+        dq, dk, dv = oracle.attention_bwd_ref(q, k, v, do, causal=causal, kv_seqlens=lens, scale=0.375)
+        fq, fk, fv = _loss_grads_fd(q, k, v, do, causal, lens, 0.375)
+        for a, b in ((dq, fq), (dk, fk), (dv, fv)):
+            assert np.allclose(a, b, rtol=0, atol=1e-8), np.abs(a - b).max()
+
+
+def check_bwd_against_autograd():
+    # torch's own attention differentiated by autograd, fp64 on the CPU
+    q, k, v, do = rand(2, 4, 9, 8), rand(2, 2, 11, 8), rand(2, 2, 11, 8), rand(2, 4, 9, 8)
+    for causal, lens in ((False, None), (True, np.array([11, 6]))):
+        qt, kt, vt = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+        Nq, Nk = 9, 11
+        i = torch.arange(Nq)[:, None]; j = torch.arange(Nk)[None, :]
+        mask = torch.ones(2, 1, Nq, Nk, dtype=torch.bool)
+        for b in range(2):
+            mb = j < (Nk if lens is None else int(lens[b]))
+            if causal:
+                mb = mb & (j <= i + (Nk - Nq))
+            mask[b, 0] = mb
+        O = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=0.25,
+                                                             enable_gqa=True)
+        (O * torch.from_numpy(do)).sum().backward()
+        dq, dk, dv = oracle.attention_bwd_ref(q, k, v, do, causal=causal, kv_seqlens=lens, scale=0.25)
+        for a, t in ((dq, qt), (dk, kt), (dv, vt)):
+            assert np.allclose(a, t.grad.numpy(), rtol=0, atol=1e-12), np.abs(a - t.grad.numpy()).max()
+
+
+def check_bwd_invariants():
+    q, k, v, do = rand(1, 4, 13, 8), rand(1, 2, 17, 8), rand(1, 2, 17, 8), rand(1, 4, 13, 8)
+    dq, dk, dv = oracle.attention_bwd_ref(q, k, v, do, causal=True, scale=0.3125)
+    # rows of dS sum to zero, so dK sums to zero over the keys
+    assert np.abs(dk.sum(axis=2)).max() < 1e-12
+    # rows of P sum to one, so dV summed over keys is dO summed over the rows
+    # (every row sees at least one key here) and the group's query heads
+    assert np.allclose(dv.sum(axis=2), do.reshape(1, 2, 2, 13, 8).sum(axis=(2, 3)), atol=1e-12)
+    # a single key: P = 1, so dS = 0 and dQ = dK = 0 while dV = sum of dO
+    q1, k1, v1, do1 = rand(1, 2, 6, 4), rand(1, 2, 1, 4), rand(1, 2, 1, 4), rand(1, 2, 6, 4)
+    dq1, dk1, dv1 = oracle.attention_bwd_ref(q1, k1, v1, do1, scale=0.5)
+    assert np.abs(dq1).max() < 1e-14 and np.abs(dk1).max() < 1e-14
+    assert np.allclose(dv1[:, :, 0], do1.sum(axis=2), atol=1e-14)
+
+
 PIN_CHECKS = [check_rows_sum_to_one, check_constant_v, check_single_key, check_causal_row0,
               check_zero_q_closed_form, check_two_keys, check_blocked_recurrence,
               check_key_permutation, check_gqa_equals_mha, check_against_torch_sdpa,
-              check_merge_identity, check_split_bounds]
+              check_merge_identity, check_split_bounds, check_bwd_finite_differences,
+              check_bwd_against_autograd, check_bwd_invariants]
 
 
 @pytest.mark.parametrize("check", PIN_CHECKS, ids=lambda f: f.__name__)
@@ -283,20 +349,55 @@ def _mut_merge_unweighted(o_parts, lse_parts):
     return np.asarray(o_parts).mean(axis=-2), lse
 
 
+def _bwd_variant(q, k, v, do, causal, kv_seqlens, scale, no_rowsum=False, unscaled_dq=False,
+                 gqa_overwrite=False):
+    q = A.to_f64(q); k = A.to_f64(k); v = A.to_f64(v); do = A.to_f64(do)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    scale = float(np.float32(scale if scale is not None else A.default_scale(d)))
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        allowed = A._allowed(Nq, Nk, A._valid_length(kv_seqlens, b, Nk), causal)
+        for hq in range(Hq):
+            hk = A._head_map(hq, Hq, Hkv)
+            o, _, P = A._one_head(q[b, hq], k[b, hk], v[b, hk], allowed, scale)
+            dP = do[b, hq] @ v[b, hk].T
+            dS = P * dP if no_rowsum else P * (dP - (do[b, hq] * o).sum(axis=1)[:, None])
+            dq[b, hq] = (1.0 if unscaled_dq else scale) * (dS @ k[b, hk])
+            if gqa_overwrite:
+                dk[b, hk] = scale * (dS.T @ q[b, hq]); dv[b, hk] = P.T @ do[b, hq]
+            else:
+                dk[b, hk] += scale * (dS.T @ q[b, hq]); dv[b, hk] += P.T @ do[b, hq]
+    return dq, dk, dv
+
+
+def _mut_bwd_no_rowsum(q, k, v, do, causal=False, kv_seqlens=None, scale=None):
+    return _bwd_variant(q, k, v, do, causal, kv_seqlens, scale, no_rowsum=True)
+
+
+def _mut_bwd_unscaled_dq(q, k, v, do, causal=False, kv_seqlens=None, scale=None):
+    return _bwd_variant(q, k, v, do, causal, kv_seqlens, scale, unscaled_dq=True)
+
+
+def _mut_bwd_gqa_overwrite(q, k, v, do, causal=False, kv_seqlens=None, scale=None):
+    return _bwd_variant(q, k, v, do, causal, kv_seqlens, scale, gqa_overwrite=True)
+
+
 _ORIG_ONE_HEAD = A._one_head
 _ORIG_MERGE = A.merge_partials
 
 MUTANTS = [("_allowed", _mut_causal_off_by_one), ("_allowed", _mut_padding_inclusive),
            ("_head_map", _mut_head_modulo), ("_one_head", _mut_lse_drops_max),
            ("_one_head", _mut_scale_twice), ("_one_head", _mut_transposed_probs),
-           ("merge_partials", _mut_merge_unweighted)]
+           ("merge_partials", _mut_merge_unweighted), ("attention_bwd_ref", _mut_bwd_no_rowsum),
+           ("attention_bwd_ref", _mut_bwd_unscaled_dq), ("attention_bwd_ref", _mut_bwd_gqa_overwrite)]
 
 
 @pytest.mark.parametrize("name,mutant", MUTANTS, ids=lambda x: getattr(x, "__name__", x))
 def test_pins_catch_planted_mistake(monkeypatch, name, mutant):
     monkeypatch.setattr(A, name, mutant)
-    if name == "merge_partials":
-        monkeypatch.setattr(oracle, "merge_partials", mutant)
+    if name in ("merge_partials", "attention_bwd_ref"):
+        monkeypatch.setattr(oracle, name, mutant)
     failed = []
     for check in PIN_CHECKS:
         try:
