@@ -101,6 +101,12 @@ def profile_only(args, dev):
         q, k, v = [t.to(dev) for t in inputs.make_inputs(3)[:3]]
         for _ in range(args.warmup + args.steps):
             fa.fa_fwd(q, k, v, causal=True)
+    elif args.only == "backward":
+        q, k, v = [t.to(dev) for t in inputs.make_inputs(3)[:3]]
+        do = inputs.make_dout(3).to(dev)
+        o, lse = fa.fa_fwd(q, k, v, causal=True)
+        for _ in range(args.warmup + args.steps):
+            fa.fa_bwd(q, k, v, o, lse, do, causal=True)
     else:
         c5 = inputs.CONFIGS[5]
         q, k, v = [t.to(dev) for t in inputs.make_inputs(5)[:3]]
@@ -117,7 +123,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100, help="untimed steps (about 0.2 s; lets clocks settle)")
     ap.add_argument("--cpu-heads", type=int, default=32, help="heads in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--bwd-steps", type=int, default=20, help="timed backward calls (0 = skip the backward)")
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "copy"], default=None,
                     help="profiling aid: run only one part of the step (or a 1 GiB device copy used to "
                          "calibrate the HBM byte counters) and print no JSON")
     args = ap.parse_args()
@@ -186,6 +193,38 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    bwd = None
+    if args.bwd_steps > 0:
+        # Backward of the same prefill (the gradients a training step needs),
+        # timed in its own loop after the step: it is reported beside the
+        # step, not folded into it.
+        do3 = inputs.make_dout(3).to(dev)
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(c3["B"], c3["Hq"], c3["Nq"], c3["d"]), dtype=torch.uint8,
+                         device=dev)
+        dq3, dk3, dv3 = torch.empty_like(q3), torch.empty_like(k3), torch.empty_like(v3)
+        print(f"[bench] backward: warmup 10, timing {args.bwd_steps}", file=sys.stderr, flush=True)
+        for _ in range(10):
+            fa.fa_bwd(q3, k3, v3, o3, l3, do3, causal=True, workspace=ws, dq=dq3, dk=dk3, dv=dv3)
+        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.bwd_steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in bev:
+            e0.record(stream)
+            fa.fa_bwd(q3, k3, v3, o3, l3, do3, causal=True, workspace=ws, dq=dq3, dk=dk3, dv=dv3)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = sum(e0.elapsed_time(e1) for e0, e1 in bev) / len(bev)
+        f_bwd = 2.5 * prefill_flops(c3["B"], c3["Hq"], c3["Nq"], c3["Nk"], c3["d"], True)
+        bwd_tf = f_bwd / (bwd_ms * 1e-3) / 1e12
+        bwd = {"value": round(bwd_tf, 2), "unit": "TFLOP/s",
+               "workload": "backward of prefill B=1 H=32 N=8192 d=128 causal bf16 (dQ, dK, dV)",
+               "flop_per_call": f_bwd, "flop_count": "5 products of 2*d FLOP per visible (query, key) pair: "
+                                                     "S recomputed, dP, dV, dK, dQ (2.5x the forward)",
+               "avg_call_ms": round(bwd_ms, 5),
+               "roofline": {"bound": "mfma", "kernel": "bwd_rowdot + bwd_dq_kernel + bwd_dkdv_kernel",
+                            "achieved": round(bwd_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+
     fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
     split_ms = [e[1].elapsed_time(e[2]) for e in events]
     merge_ms = [e[2].elapsed_time(e[3]) for e in events]
@@ -240,6 +279,7 @@ def main():
                          "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                          "traffic": load_traffic("decode_splitkv_bf16_kernel+lse_merge_kernel")},
         },
+        "backward": bwd,
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

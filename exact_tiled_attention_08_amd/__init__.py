@@ -1,4 +1,4 @@
-"""Exact tiled attention (prefill forward, split-KV decode, LSE merge) on gfx950.
+"""Exact tiled attention (prefill forward and backward, split-KV decode, LSE merge) on gfx950.
 
 Thin torch-facing wrappers over the C ABI in include/fa.h.  Each function has
 the name of the C entry point it marshals arguments for; all computation runs
@@ -13,7 +13,8 @@ from . import _lib
 from ._lib import FAError, FA_DECODE_SPLIT_ALIGN, FA_MAX_SPLITS  # noqa: F401
 
 __all__ = ["fa_fwd", "fa_decode_splitkv", "fa_lse_merge", "fa_decode", "fa_decode_workspace_bytes",
-           "fa_status_string", "fa_last_error", "FAError", "default_scale"]
+           "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_last_error", "FAError",
+           "default_scale"]
 
 _DTYPES = {torch.bfloat16: _lib.FA_BF16, torch.float32: _lib.FA_F32}
 
@@ -173,6 +174,46 @@ def fa_decode(q, k_cache, v_cache, kv_seqlens=None, num_splits=16, scale=None, w
                              s, _ptr(lens), num_splits, _ptr(workspace), workspace.numel(),
                              _DTYPES[q.dtype], _stream(q)))
     return out, lse
+
+
+def fa_bwd_workspace_bytes(B, Hq, Nq, d):
+    return int(_lib.load().fa_bwd_workspace_bytes(B, Hq, Nq, d))
+
+
+def fa_bwd(q, k, v, o, lse, dout, causal=False, kv_seqlens=None, scale=None, workspace=None,
+           dq=None, dk=None, dv=None):
+    """Gradients of fa_fwd: given its inputs, its outputs (o, lse) and dout = dL/dO, returns
+    (dq, dk, dv) shaped like q, k, v (bf16 only)."""
+    _check_tensor(q, "q", torch.bfloat16, 4)
+    for t, name in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check_tensor(t, name, torch.bfloat16, 4, q.device)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, Hkv, Nk, d] matching q")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o and dout must be shaped like q")
+    _check_tensor(lse, "lse", torch.float32, 3, q.device)
+    if tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("lse must be [B, Hq, Nq]")
+    lens = _lens(kv_seqlens, B, q.device)
+    lib = _lib.load()
+    need = int(lib.fa_bwd_workspace_bytes(B, Hq, Nq, d))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_tensor(workspace, "workspace", torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, ref, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _check_tensor(t, name, torch.bfloat16, 4, q.device)
+        if tuple(t.shape) != tuple(ref.shape):
+            raise ValueError(f"{name} has the wrong shape")
+    s = default_scale(d) if scale is None else float(scale)
+    _lib.check(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                          _ptr(dv), B, Hq, Hkv, Nq, Nk, d, s, int(bool(causal)), _ptr(lens), _ptr(workspace),
+                          workspace.numel(), _lib.FA_BF16, _stream(q)))
+    return dq, dk, dv
 
 
 def fa_status_string(status):

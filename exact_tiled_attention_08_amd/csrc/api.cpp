@@ -198,4 +198,53 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, 
                     "fa_decode merge stage launch");
 }
 
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq, int d) {
+  if (B < 0 || Hq < 0 || Nq < 0 || (d != 64 && d != 128)) return 0;
+  return ((size_t)B * Hq * Nq * sizeof(float) + 255) / 256 * 256;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+           const int32_t* kv_seqlens, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  int st = check_common(B, Hq, Hkv, Nq, Nk, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "fa_bwd supports bf16 only");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  const bool has_q = (long long)B * Hq * Nq > 0, has_k = (long long)B * Hkv * Nk > 0;
+  if (!has_q && !has_k) return ok();  // nothing to write
+  if (has_q) {
+    if ((st = check_ptr(q, 16, "q")) != FA_OK) return st;
+    if ((st = check_ptr(o, 16, "o")) != FA_OK) return st;
+    if ((st = check_ptr(dout, 16, "dout")) != FA_OK) return st;
+    if ((st = check_ptr(lse, 4, "lse")) != FA_OK) return st;
+    if ((st = check_ptr(dq, 16, "dq")) != FA_OK) return st;
+    const size_t need = fa_bwd_workspace_bytes(B, Hq, Nq, d);
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  }
+  if (has_k) {
+    if ((st = check_ptr(k, 16, "k")) != FA_OK) return st;
+    if ((st = check_ptr(v, 16, "v")) != FA_OK) return st;
+    if ((st = check_ptr(dk, 16, "dk")) != FA_OK) return st;
+    if ((st = check_ptr(dv, 16, "dv")) != FA_OK) return st;
+  }
+  if (kv_seqlens != nullptr && !aligned(kv_seqlens, 4))
+    return fail(FA_ERR_INVALID_ARG, "kv_seqlens is not 4-byte aligned");
+  const long long qtiles = ((long long)Nq + 127) / 128 * B * Hq, ktiles = ((long long)Nk + 127) / 128 * B * Hkv;
+  if (qtiles > 0x7fffffffLL || ktiles > 0x7fffffffLL || (long long)B * Hq * Nq > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "problem too large for one launch");
+  fa::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.rowdot = (float*)workspace;
+  a.kv_seqlens = kv_seqlens;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.d = d;
+  a.scale = scale;
+  a.causal = causal;
+  a.stream = (hipStream_t)stream;
+  return hip_status(fa::launch_bwd_bf16(a), "fa_bwd launch");
+}
+
 }  // extern "C"

@@ -1,0 +1,406 @@
+// Backward pass of exact attention (bf16, matrix cores): dQ, dK, dV.
+//
+// The pages say that the backward pass recomputes intermediate values instead
+// of storing them (Exam deep-dive "Flash Attention 在改善什麼？", section 技術版,
+// "Recomputation"; Interview note, section 节省显存，不等于所有内存都变少).  What
+// it computes is the derivative of the forward definition of the "FlashAttention"
+// concept note, section "是什么".  Per (query i, key j) pair that takes part:
+//     P_ij  = 2^(S_ij * scale * log2(e) - LSE_i * log2(e))     (recomputed)
+//     dP_ij = dO_i . V_j
+//     dS_ij = P_ij (dP_ij - D_i),   D_i = dO_i . O_i
+//     dV_j += P_ij dO_i,   dK_j += scale dS_ij Q_i,   dQ_i += scale dS_ij K_j
+// Three kernels: D (one dot product per query row), dQ (one work-group per
+// 128-query block streaming 32-key tiles), and dK/dV (one work-group per
+// 128-key block streaming the 32-query tiles of every query head that reads
+// it).  The two gradient kernels keep different operands on the lanes -- dQ
+// the queries (as in the forward), dK/dV the keys -- so every product takes
+// its operands straight from the recomputed tiles: no atomics and no extra
+// transposes beyond the ds_read_b64_tr_b16 reads already used by the forward.
+#include "fa_device.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+// Element offset of (row, 16-byte chunk) in a row-major [rows][D] bf16 tile
+// whose chunks are XOR-swizzled per row.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+  return row * D + ((chunk ^ swz<D>(row)) * 8);
+}
+
+// Register-staged copy of an R-row tile: load() reads rows [0, nvalid) of a
+// row-major [*, D] bf16 tensor (later rows become zeros), store() writes the
+// swizzled tile to LDS.  256 threads; consecutive threads take consecutive
+// 16-byte chunks of a row.
+template <int D, int R>
+struct TileStage {
+  static constexpr int CPR = D / 8;
+  static constexpr int CH = R * CPR / 256;
+  static_assert(CH >= 1 && R * CPR % 256 == 0, "tile must split evenly over 256 threads");
+  uint4 reg[CH];
+  __device__ __forceinline__ void load(const uint16_t* base, int nvalid, int tid) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + c * 256, row = idx / CPR, ch = idx % CPR;
+      reg[c] = row < nvalid ? *(const uint4*)(base + (size_t)row * D + ch * 8) : uint4{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + c * 256, row = idx / CPR, ch = idx % CPR;
+      *(uint4*)(lds + tile_off<D>(row, ch)) = reg[c];
+    }
+  }
+};
+
+// A operand of an MFMA whose rows are the tile's columns (d) and whose k runs
+// over 16 tile rows starting at r0: two ds_read_b64_tr_b16 (rows r0 + tr_r and
+// r0 + 8 + tr_r).  Lane l supplies d = 32*db + (l % 32); the k order matches
+// that of a 32x32 accumulator's registers 8*mm .. 8*mm+7 turned into a bf16x8
+// B operand (rows 8*(t/4) + 4*(l/32) + t%4 of the slice), as in the forward.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_fragment(const uint16_t* tile, int r0, int db, int lane) {
+  const int tr_r = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_in = 4 * (lane & 1);
+  const int ch = 4 * db + tr_cc;
+  return join_bf16x8(lds_read_tr16(tile + tile_off<D>(r0 + tr_r, ch) + tr_in),
+                     lds_read_tr16(tile + tile_off<D>(r0 + 8 + tr_r, ch) + tr_in));
+}
+
+// ---------------------------------------------------------------------------
+// D_i = dO_i . O_i (float32), one row per TPR threads.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restrict__ dout,
+                                                          const uint16_t* __restrict__ o, float* __restrict__ rowdot,
+                                                          long long rows) {
+  constexpr int TPR = D / 8;  // threads per row, 8 elements each
+  const long long row = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int sub = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint4 a = *(const uint4*)(dout + row * D + sub * 8);
+    const uint4 b = *(const uint4*)(o + row * D + sub * 8);
+    const unsigned ua[4] = {a.x, a.y, a.z, a.w}, ub[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      acc = __builtin_fmaf(__uint_as_float(ua[x] << 16), __uint_as_float(ub[x] << 16), acc);
+      acc = __builtin_fmaf(__uint_as_float(ua[x] & 0xffff0000u), __uint_as_float(ub[x] & 0xffff0000u), acc);
+    }
+  }
+#pragma unroll
+  for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (row < rows && sub == 0) rowdot[row] = acc;
+}
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* lse;
+  const float* rowdot;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  const int32_t* kv_seqlens;
+  int B, Hq, Hkv, Nq, Nk;
+  int n_tiles;       // query blocks (dQ kernel) or key blocks (dK/dV kernel) per head
+  float scale;
+  float scale_log2;  // scale * log2(e)
+};
+
+// LSE in base 2 for the recomputation of P; a row with no visible key (LSE =
+// -inf) gets +inf so that every recomputed probability of the row is 0.
+__device__ __forceinline__ float lse_base2(float lse) { return lse == kNegInf ? __builtin_inff() : lse * kLog2e; }
+
+// ---------------------------------------------------------------------------
+// dQ: 4 waves x 32 query rows per work-group; 32-key tiles.  Per tile and wave
+//   S^T  = K Q^T,  dP^T = V dO^T           (A: K / V rows from LDS, B: Q / dO in VGPRs)
+//   dS^T = P^T * (dP^T - D)                (P^T recomputed from the LSE)
+//   dQ^T += K^T dS^T                       (A: K^T by transposed reads, B: dS^T)
+template <int D, bool CAUSAL, bool PADDED>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
+  constexpr int BM = 128, BN = 32;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[BN * D];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, li = lane & 31, hi = lane >> 5;
+  const int bh_count = p.B * p.Hq;
+  const int bh = blockIdx.x % bh_count;
+  const int qt = p.n_tiles - 1 - (int)(blockIdx.x / bh_count);  // heaviest (causal) first
+  const int b = bh / p.Hq, hq = bh - b * p.Hq;
+  const int hk = hq / (p.Hq / p.Hkv);
+
+  const int kv_len = PADDED ? clamp_len(p.kv_seqlens, b, p.Nk) : p.Nk;
+  const int q0 = qt * BM;
+  const int diag = p.Nk - p.Nq;
+  int kend = kv_len;
+  if (CAUSAL) kend = min(kend, min(q0 + BM, p.Nq) - 1 + diag + 1);
+  const int n_kt = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+  const size_t qrow_base = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
+  const size_t kv_base = ((size_t)b * p.Hkv + hk) * (size_t)p.Nk;
+  const int qrow = q0 + wave * 32 + li;
+  const bool row_ok = qrow < p.Nq;
+
+  bf16x8 qf[D / 16], dof[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    if (row_ok) {
+      qf[st] = *(const bf16x8*)(p.q + (qrow_base + qrow) * D + 16 * st + 8 * hi);
+      dof[st] = *(const bf16x8*)(p.dout + (qrow_base + qrow) * D + 16 * st + 8 * hi);
+    } else {
+      qf[st] = bf16x8{};
+      dof[st] = bf16x8{};
+    }
+  }
+  const float lse2 = row_ok ? lse_base2(p.lse[qrow_base + qrow]) : __builtin_inff();
+  const float drow = row_ok ? p.rowdot[qrow_base + qrow] : 0.f;
+
+  f32x16 dq_acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dq_acc[db] = f32x16{};
+
+  TileStage<D, BN> kst, vst;
+  const uint16_t* kg = p.k + kv_base * D;
+  const uint16_t* vg = p.v + kv_base * D;
+  if (n_kt > 0) {
+    kst.load(kg, kv_len, tid);
+    vst.load(vg, kv_len, tid);
+  }
+  for (int t = 0; t < n_kt; ++t) {
+    __syncthreads();
+    kst.store(k_lds, tid);
+    vst.store(v_lds, tid);
+    __syncthreads();
+    if (t + 1 < n_kt) {
+      const int k1 = (t + 1) * BN;
+      kst.load(kg + (size_t)k1 * D, kv_len - k1, tid);
+      vst.load(vg + (size_t)k1 * D, kv_len - k1, tid);
+    }
+    const int k0 = t * BN;
+
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      s = mfma32x32x16(*(const bf16x8*)(k_lds + tile_off<D>(li, 2 * st + hi)), qf[st], s);
+      dp = mfma32x32x16(*(const bf16x8*)(v_lds + tile_off<D>(li, 2 * st + hi)), dof[st], dp);
+    }
+    // lane l: query qrow; register r: key k0 + 8(r/4) + 4*hi + r%4
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      bool vis = key < kv_len;
+      if (CAUSAL) vis = vis && key <= qrow + diag;
+      const float pr = vis ? fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -lse2)) : 0.f;
+      ds[r] = pr * (dp[r] - drow);
+    }
+    bf16x8 dsf[2];
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) dsf[mm] = pack_bf16x8(ds + 8 * mm);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) dq_acc[db] = mfma32x32x16(tr_fragment<D>(k_lds, 16 * mm, db, lane), dsf[mm], dq_acc[db]);
+  }
+
+  if (row_ok) {
+    uint16_t* op = p.dq + (qrow_base + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 w;
+        w.x = pack_bf16x2(dq_acc[db][4 * g] * p.scale, dq_acc[db][4 * g + 1] * p.scale);
+        w.y = pack_bf16x2(dq_acc[db][4 * g + 2] * p.scale, dq_acc[db][4 * g + 3] * p.scale);
+        *(uint2*)(op + db * 32 + 8 * g + 4 * hi) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: 4 waves x 32 keys per work-group (the block's K and V stay in LDS);
+// 32-query tiles of every query head that reads this KV head.  Per tile and
+// wave, with the keys on the lanes:
+//   S  = Q K^T,  dP = dO V^T                (A: Q / dO rows, B: K / V rows, all from LDS)
+//   dS = P * (dP - D)                       (P recomputed from the LSE)
+//   dV^T += dO^T P,  dK^T += Q^T dS         (A: transposed reads of dO / Q, B: P / dS)
+template <int D, bool CAUSAL, bool PADDED>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int BK = 128, BQ = 32;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[BK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[BQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t do_lds[BQ * D];
+  __shared__ __attribute__((aligned(16))) float lse_lds[BQ];
+  __shared__ __attribute__((aligned(16))) float d_lds[BQ];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, li = lane & 31, hi = lane >> 5;
+  const int bh_count = p.B * p.Hkv;
+  const int bh = blockIdx.x % bh_count;
+  const int kt = (int)(blockIdx.x / bh_count);  // causal: the first key blocks carry the most work
+  const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
+  const int group = p.Hq / p.Hkv;
+
+  const int kv_len = PADDED ? clamp_len(p.kv_seqlens, b, p.Nk) : p.Nk;
+  const int kt0 = kt * BK;
+  const int diag = p.Nk - p.Nq;
+  const size_t kv_base = ((size_t)b * p.Hkv + hk) * (size_t)p.Nk;
+  const int key = kt0 + wave * 32 + li;  // this lane's key (both halves)
+
+  {
+    TileStage<D, BK> kst, vst;
+    kst.load(p.k + (kv_base + kt0) * D, kv_len - kt0, tid);
+    vst.load(p.v + (kv_base + kt0) * D, kv_len - kt0, tid);
+    kst.store(k_lds, tid);
+    vst.store(v_lds, tid);
+  }
+
+  // Query tiles that can see a key of this block: all of them, from the one
+  // holding row kt0 - diag on under the causal mask; none if the block lies
+  // wholly past the sequence's length.
+  int qt_first = 0;
+  if (CAUSAL) qt_first = max(0, kt0 - diag) / BQ;
+  const int n_qt = (p.Nq + BQ - 1) / BQ;
+  const int per_head = kt0 < kv_len ? max(0, n_qt - qt_first) : 0;
+  const int n_it = per_head * group;
+
+  f32x16 dk_acc[D / 32], dv_acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dk_acc[db] = dv_acc[db] = f32x16{};
+
+  TileStage<D, BQ> qst, dost;
+  float lse_r = 0.f, d_r = 0.f;  // staged by threads 0 .. BQ-1
+  auto load_it = [&](int it) {
+    const int hq = hk * group + it / per_head;
+    const int q0 = (qt_first + it % per_head) * BQ;
+    const size_t rb = ((size_t)b * p.Hq + hq) * (size_t)p.Nq + q0;
+    qst.load(p.q + rb * D, p.Nq - q0, tid);
+    dost.load(p.dout + rb * D, p.Nq - q0, tid);
+    if (tid < BQ) {
+      const bool ok = q0 + tid < p.Nq;
+      lse_r = ok ? lse_base2(p.lse[rb + tid]) : __builtin_inff();
+      d_r = ok ? p.rowdot[rb + tid] : 0.f;
+    }
+  };
+  if (n_it > 0) load_it(0);
+  for (int it = 0; it < n_it; ++it) {
+    __syncthreads();
+    qst.store(q_lds, tid);
+    dost.store(do_lds, tid);
+    if (tid < BQ) {
+      lse_lds[tid] = lse_r;
+      d_lds[tid] = d_r;
+    }
+    __syncthreads();
+    const int q0 = (qt_first + it % per_head) * BQ;
+    if (it + 1 < n_it) load_it(it + 1);
+
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      const int kr = wave * 32 + li;
+      s = mfma32x32x16(*(const bf16x8*)(q_lds + tile_off<D>(li, 2 * st + hi)),
+                       *(const bf16x8*)(k_lds + tile_off<D>(kr, 2 * st + hi)), s);
+      dp = mfma32x32x16(*(const bf16x8*)(do_lds + tile_off<D>(li, 2 * st + hi)),
+                        *(const bf16x8*)(v_lds + tile_off<D>(kr, 2 * st + hi)), dp);
+    }
+    // lane l: key `key`; register r: query q0 + 8(r/4) + 4*hi + r%4
+    float pr[16], ds[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 lv = *(const float4*)(lse_lds + 8 * j + 4 * hi);
+      const float4 dv4 = *(const float4*)(d_lds + 8 * j + 4 * hi);
+      const float lse4[4] = {lv.x, lv.y, lv.z, lv.w}, d4[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = 4 * j + x;
+        const int q = q0 + 8 * j + 4 * hi + x;
+        bool vis = key < kv_len && q < p.Nq;
+        if (CAUSAL) vis = vis && key <= q + diag;
+        pr[r] = vis ? fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -lse4[x])) : 0.f;
+        ds[r] = pr[r] * (dp[r] - d4[x]);
+      }
+    }
+    bf16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      pf[mm] = pack_bf16x8(pr + 8 * mm);
+      dsf[mm] = pack_bf16x8(ds + 8 * mm);
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        dv_acc[db] = mfma32x32x16(tr_fragment<D>(do_lds, 16 * mm, db, lane), pf[mm], dv_acc[db]);
+        dk_acc[db] = mfma32x32x16(tr_fragment<D>(q_lds, 16 * mm, db, lane), dsf[mm], dk_acc[db]);
+      }
+  }
+
+  if (key < p.Nk) {
+    uint16_t* kp = p.dk + (kv_base + key) * D;
+    uint16_t* vp = p.dv + (kv_base + key) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 wk, wv;
+        wk.x = pack_bf16x2(dk_acc[db][4 * g] * p.scale, dk_acc[db][4 * g + 1] * p.scale);
+        wk.y = pack_bf16x2(dk_acc[db][4 * g + 2] * p.scale, dk_acc[db][4 * g + 3] * p.scale);
+        wv.x = pack_bf16x2(dv_acc[db][4 * g], dv_acc[db][4 * g + 1]);
+        wv.y = pack_bf16x2(dv_acc[db][4 * g + 2], dv_acc[db][4 * g + 3]);
+        *(uint2*)(kp + db * 32 + 8 * g + 4 * hi) = wk;
+        *(uint2*)(vp + db * 32 + 8 * g + 4 * hi) = wv;
+      }
+  }
+}
+
+template <int D, bool CAUSAL, bool PADDED>
+static hipError_t launch_bwd_t(const BwdArgs& a) {
+  BwdParams p;
+  p.q = (const uint16_t*)a.q;
+  p.k = (const uint16_t*)a.k;
+  p.v = (const uint16_t*)a.v;
+  p.dout = (const uint16_t*)a.dout;
+  p.lse = a.lse;
+  p.rowdot = a.rowdot;
+  p.dq = (uint16_t*)a.dq;
+  p.dk = (uint16_t*)a.dk;
+  p.dv = (uint16_t*)a.dv;
+  p.kv_seqlens = a.kv_seqlens;
+  p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
+  p.scale = a.scale;
+  p.scale_log2 = a.scale * kLog2e;
+  const long long rows = (long long)a.B * a.Hq * a.Nq;
+  if (rows > 0) {
+    constexpr int RPB = 256 / (D / 8);
+    hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, a.stream,
+                       (const uint16_t*)a.dout, (const uint16_t*)a.o, a.rowdot, rows);
+    p.n_tiles = (a.Nq + 127) / 128;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PADDED>), dim3((unsigned)((long long)p.n_tiles * a.B * a.Hq)),
+                       dim3(256), 0, a.stream, p);
+  }
+  const long long krows = (long long)a.B * a.Hkv * a.Nk;
+  if (krows > 0) {
+    p.n_tiles = (a.Nk + 127) / 128;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, PADDED>), dim3((unsigned)((long long)p.n_tiles * a.B * a.Hkv)),
+                       dim3(256), 0, a.stream, p);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_d(const BwdArgs& a) {
+  const bool padded = a.kv_seqlens != nullptr;
+  if (a.causal) return padded ? launch_bwd_t<D, true, true>(a) : launch_bwd_t<D, true, false>(a);
+  return padded ? launch_bwd_t<D, false, true>(a) : launch_bwd_t<D, false, false>(a);
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& a) { return a.d == 128 ? launch_bwd_d<128>(a) : launch_bwd_d<64>(a); }
+
+}  // namespace fa

@@ -37,6 +37,26 @@ hipError_t launch_decode_splitkv_bf16(const AttnArgs& a, const PartialOut& part)
 hipError_t launch_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
                             int rows, int d, int num_splits, bool out_bf16, hipStream_t stream);
 
+// Backward pass (bf16): gradients of fa_fwd's output.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* rowdot;  // workspace: rowsum(dO * O) per query row, [B, Hq, Nq]
+  const int32_t* kv_seqlens;
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+  hipStream_t stream;
+};
+hipError_t launch_bwd_bf16(const BwdArgs& a);
+
 // Split-KV chunk length for a sequence of `len` valid keys.
 __host__ __device__ inline int split_chunk(int len, int num_splits, int align) {
   if (len <= 0) return 0;

@@ -12,7 +12,7 @@ import os
 
 import torch
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_LENS = 0, 1, 2, 3
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_LENS, TENSOR_DOUT = 0, 1, 2, 3, 4
 
 # The five workloads.  "N" is both Nq and Nk for prefill; decode has Nq = 1.
 CONFIGS = {
@@ -91,3 +91,11 @@ def make_inputs(config_id, *, B=None, Hq=None, Hkv=None, Nq=None, Nk=None, d=Non
         hi = c.get("len_hi", c["Nk"])
         lens = lengths(config_id, c["B"], lo, hi)
     return q, k, v, lens
+
+
+def make_dout(config_id, **overrides):
+    """Seeded upstream gradient dL/dO shaped like a config's q (same value
+    distribution as q), for the backward pass."""
+    c = dict(CONFIGS[config_id])
+    c.update({k: v for k, v in overrides.items() if v is not None})
+    return randn_tensor(config_id, TENSOR_DOUT, c["B"], c["Hq"], c["Nq"], c["d"], c["mult"], c["dtype"])

@@ -55,7 +55,7 @@ enum fa_status {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1, /* null / misaligned pointer, negative size, bad scale */
   FA_ERR_UNSUPPORTED = -2, /* d, dtype, head ratio or num_splits outside the supported set */
-  FA_ERR_WORKSPACE = -3,   /* decode workspace missing or smaller than fa_decode_workspace_bytes */
+  FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than fa_decode_workspace_bytes / fa_bwd_workspace_bytes */
   FA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
 };
 
@@ -135,6 +135,41 @@ int fa_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse
 int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
               int B, int Hq, int Hkv, int Nk, int d, float scale, const int32_t* kv_seqlens,
               int num_splits, void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * fa_bwd_workspace_bytes -- bytes of device workspace fa_bwd needs: one
+ * float32 per query row, [B, Hq, Nq] (rowsum(dO * O)).  Returns 0 for
+ * invalid arguments.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq, int d);
+
+/*
+ * fa_bwd -- gradients of fa_fwd's output for training: given dO = dL/dO,
+ * computes dQ, dK, dV of the loss L.  The backward pass recomputes the score
+ * and probability tiles from Q, K and the forward's LSE instead of storing
+ * them (Exam deep-dive "Flash Attention 在改善什麼？", section 技術版,
+ * "Recomputation"; Interview note, section 节省显存，不等于所有内存都变少); what
+ * it computes is the derivative of the forward definition:
+ *     dV = P^T dO,   dS = P * (dO V^T - rowsum(dO * O)),
+ *     dQ = scale * dS K,   dK = scale * dS^T Q,
+ * with P = softmax(scale * Q K^T) under the same masks as fa_fwd (disallowed
+ * pairs contribute nothing) and, with GQA, dK/dV summed over the query heads
+ * that share a KV head.
+ *   q, o, dout [B,Hq,Nq,d] bf16 in; k, v [B,Hkv,Nk,d] bf16 in;
+ *   lse [B,Hq,Nq] float32 in: exactly what fa_fwd returned for these inputs;
+ *   dq [B,Hq,Nq,d], dk, dv [B,Hkv,Nk,d] bf16 out (fully written: key rows at
+ *   or beyond a sequence's length and rows with no visible key get zeros);
+ *   causal, kv_seqlens, scale as for fa_fwd;
+ *   workspace: device memory of at least fa_bwd_workspace_bytes(B, Hq, Nq, d)
+ *   bytes, 256-byte aligned, overwritten.
+ * Only dtype FA_BF16 is supported (FA_F32 returns FA_ERR_UNSUPPORTED); dO and
+ * dS are rounded to bf16 before their matrix-core products, accumulation is
+ * float32.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk,
+           int d, float scale, int causal, const int32_t* kv_seqlens, void* workspace,
+           size_t workspace_bytes, int dtype, void* stream);
 
 /* Static string for a status code. */
 const char* fa_status_string(int status);

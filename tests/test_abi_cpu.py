@@ -116,3 +116,38 @@ def test_python_binding_requires_gpu_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fa_fwd(q, q, q)
+
+
+def bwd(lib, q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Nq=16, Nk=16, d=128,
+        scale=0.1, causal=1, lens=None, ws=P, ws_bytes=None, dtype=1):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_bytes(max(B, 0), max(Hq, 0), max(Nq, 0), d) if d in (64, 128) else 0
+    return lib.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale, causal, lens, ws, ws_bytes,
+                      dtype, None)
+
+
+def test_bwd_workspace_bytes(lib):
+    assert lib.fa_bwd_workspace_bytes(1, 32, 8192, 128) == 32 * 8192 * 4
+    assert lib.fa_bwd_workspace_bytes(1, 1, 3, 64) == 256
+    assert lib.fa_bwd_workspace_bytes(1, 1, 4, 96) == 0
+    assert lib.fa_bwd_workspace_bytes(-1, 1, 4, 64) == 0
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=0), UNSUP), (dict(dtype=3), UNSUP), (dict(d=96), UNSUP), (dict(Hq=3), UNSUP),
+    (dict(q=None), BAD), (dict(o=None), BAD), (dict(do=None), BAD), (dict(lse=None), BAD),
+    (dict(dq=None), BAD), (dict(dk=None), BAD), (dict(dv=None), BAD), (dict(k=P + 8), BAD),
+    (dict(ws=None), WS), (dict(ws_bytes=100), WS), (dict(ws=P + 64), BAD), (dict(causal=5), BAD),
+    (dict(scale=0.0), BAD), (dict(lens=P + 2), BAD), (dict(Nk=-1), BAD),
+])
+def test_bwd_rejects(lib, kwargs, status):
+    assert bwd(lib, **kwargs) == status
+    assert lib.fa_last_error() != b""
+
+
+def test_bwd_empty_is_noop(lib):
+    # nothing to write at all
+    assert bwd(lib, B=0, q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None,
+               ws=None) == _lib.FA_OK
+    assert bwd(lib, Hq=0, Hkv=0, q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None,
+               ws=None) == _lib.FA_OK
