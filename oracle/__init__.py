@@ -19,5 +19,6 @@ from .attention import (  # noqa: F401
     split_bounds,
     decode_partials_ref,
     score_matrix_bytes,
+    paged_to_contiguous,
     to_f64,
 )

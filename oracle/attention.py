@@ -308,6 +308,32 @@ def decode_partials_ref(q, k, v, kv_seqlens, scale, num_splits, tile):
     return O, LSE
 
 
+def paged_to_contiguous(pages, block_table, lengths, page_size):
+    """Gather a paged KV cache into contiguous per-sequence rows.
+
+    The pages place the KV cache under page management (PagedAttention) and
+    leave the layout open (Concept note, section "是什么", table of related
+    concepts).  The plainest reading, used here: pages is a pool
+    [num_pages, Hkv, page_size, d]; block_table[b] lists sequence b's pages
+    in key order, so key j of sequence b is row j % page_size of page
+    block_table[b][j // page_size].  Returns [B, Hkv, max_pages * page_size, d]
+    with the rows at or beyond lengths[b] set to NaN (they must never be read).
+    """
+    pages = to_f64(pages)
+    table = np.asarray(to_f64(block_table), dtype=np.int64)
+    lengths = np.asarray(to_f64(lengths), dtype=np.int64)
+    B, max_pages = table.shape
+    _, Hkv, P, d = pages.shape
+    if P != page_size:
+        raise ValueError("page_size does not match the pool")
+    out = np.full((B, Hkv, max_pages * P, d), np.nan)
+    for b in range(B):
+        L = int(min(max(lengths[b], 0), max_pages * P))
+        for j in range(L):
+            out[b, :, j] = pages[table[b, j // P], :, j % P]
+    return out
+
+
 def score_matrix_bytes(n, bytes_per_element):
     """Bytes of one materialised n x n score (or probability) matrix."""
     return n * n * bytes_per_element

@@ -269,11 +269,36 @@ def check_bwd_invariants():
     assert np.allclose(dv1[:, :, 0], do1.sum(axis=2), atol=1e-14)
 
 
+def check_paged_gather():
+    # scatter a known contiguous cache into a shuffled page pool (one page per
+    # page_size keys, in a random order, plus unused pages), gather it back
+    rng = np.random.default_rng(5)
+    B, Hkv, P, d, max_pages = 3, 2, 4, 5, 6
+    contig = rng.standard_normal((B, Hkv, max_pages * P, d))
+    lengths = np.array([24, 9, 0])
+    n_pages = B * max_pages + 3
+    perm = rng.permutation(n_pages)[:B * max_pages].reshape(B, max_pages)
+    pool = rng.standard_normal((n_pages, Hkv, P, d))
+    for b in range(B):
+        for t in range(max_pages):
+            pool[perm[b, t]] = contig[b, :, t * P:(t + 1) * P]
+    got = oracle.paged_to_contiguous(pool, perm, lengths, P)
+    for b in range(B):
+        L = lengths[b]
+        assert np.array_equal(got[b, :, :L], contig[b, :, :L])
+        assert np.isnan(got[b, :, L:]).all()
+    # attention over the gathered keys equals attention over the original cache
+    q = rng.standard_normal((B, 4, 1, d))
+    O1, L1 = oracle.attention_ref(q, np.nan_to_num(got), np.nan_to_num(got), kv_seqlens=lengths, scale=0.5)
+    O2, L2 = oracle.attention_ref(q, contig, contig, kv_seqlens=lengths, scale=0.5)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
 PIN_CHECKS = [check_rows_sum_to_one, check_constant_v, check_single_key, check_causal_row0,
               check_zero_q_closed_form, check_two_keys, check_blocked_recurrence,
               check_key_permutation, check_gqa_equals_mha, check_against_torch_sdpa,
               check_merge_identity, check_split_bounds, check_bwd_finite_differences,
-              check_bwd_against_autograd, check_bwd_invariants]
+              check_bwd_against_autograd, check_bwd_invariants, check_paged_gather]
 
 
 @pytest.mark.parametrize("check", PIN_CHECKS, ids=lambda f: f.__name__)
@@ -383,6 +408,15 @@ def _mut_bwd_gqa_overwrite(q, k, v, do, causal=False, kv_seqlens=None, scale=Non
     return _bwd_variant(q, k, v, do, causal, kv_seqlens, scale, gqa_overwrite=True)
 
 
+def _mut_paged_row_reversed(pages, block_table, lengths, page_size):
+    out = _ORIG_PAGED(pages, block_table, lengths, page_size)
+    P = page_size
+    for j0 in range(0, out.shape[2], P):
+        out[:, :, j0:j0 + P] = out[:, :, j0:j0 + P][:, :, ::-1]
+    return out
+
+
+_ORIG_PAGED = A.paged_to_contiguous
 _ORIG_ONE_HEAD = A._one_head
 _ORIG_MERGE = A.merge_partials
 
@@ -390,13 +424,14 @@ MUTANTS = [("_allowed", _mut_causal_off_by_one), ("_allowed", _mut_padding_inclu
            ("_head_map", _mut_head_modulo), ("_one_head", _mut_lse_drops_max),
            ("_one_head", _mut_scale_twice), ("_one_head", _mut_transposed_probs),
            ("merge_partials", _mut_merge_unweighted), ("attention_bwd_ref", _mut_bwd_no_rowsum),
-           ("attention_bwd_ref", _mut_bwd_unscaled_dq), ("attention_bwd_ref", _mut_bwd_gqa_overwrite)]
+           ("attention_bwd_ref", _mut_bwd_unscaled_dq), ("attention_bwd_ref", _mut_bwd_gqa_overwrite),
+           ("paged_to_contiguous", _mut_paged_row_reversed)]
 
 
 @pytest.mark.parametrize("name,mutant", MUTANTS, ids=lambda x: getattr(x, "__name__", x))
 def test_pins_catch_planted_mistake(monkeypatch, name, mutant):
     monkeypatch.setattr(A, name, mutant)
-    if name in ("merge_partials", "attention_bwd_ref"):
+    if name in ("merge_partials", "attention_bwd_ref", "paged_to_contiguous"):
         monkeypatch.setattr(oracle, name, mutant)
     failed = []
     for check in PIN_CHECKS:
