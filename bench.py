@@ -124,6 +124,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=32, help="heads in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=20, help="timed backward calls (0 = skip the backward)")
+    ap.add_argument("--paged-steps", type=int, default=20,
+                    help="timed paged-cache decode calls (0 = skip the paged decode)")
     ap.add_argument("--only", choices=["prefill", "decode", "backward", "copy"], default=None,
                     help="profiling aid: run only one part of the step (or a 1 GiB device copy used to "
                          "calibrate the HBM byte counters) and print no JSON")
@@ -225,6 +227,43 @@ def main():
                             "achieved": round(bwd_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
 
+    paged = None
+    if args.paged_steps > 0:
+        # The same decode over a paged copy of the cache: 16-key pages in a
+        # shuffled pool, read through a block table.
+        page = 16
+        n_pages = B5 * (Nk5 // page)
+        g = torch.Generator(device=dev).manual_seed(555)
+        table = torch.randperm(n_pages, generator=g, device=dev).to(torch.int32).reshape(B5, Nk5 // page)
+        kp = torch.empty((n_pages, Hkv5, page, d5), dtype=torch.bfloat16, device=dev)
+        vp = torch.empty_like(kp)
+        idx = table.long().reshape(-1)
+        kp[idx] = k5.reshape(B5, Hkv5, Nk5 // page, page, d5).permute(0, 2, 1, 3, 4).reshape(-1, Hkv5, page, d5)
+        vp[idx] = v5.reshape(B5, Hkv5, Nk5 // page, page, d5).permute(0, 2, 1, 3, 4).reshape(-1, Hkv5, page, d5)
+        lens5 = torch.full((B5,), Nk5, dtype=torch.int32, device=dev)
+        wsp = torch.empty(fa.fa_decode_workspace_bytes(B5, Hq5, d5, S), dtype=torch.uint8, device=dev)
+        print(f"[bench] paged decode: warmup 10, timing {args.paged_steps}", file=sys.stderr, flush=True)
+        for _ in range(10):
+            fa.fa_decode_paged(q5, kp, vp, table, lens5, num_splits=S, workspace=wsp, out=o5, lse=l5)
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.paged_steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in pev:
+            e0.record(stream)
+            fa.fa_decode_paged(q5, kp, vp, table, lens5, num_splits=S, workspace=wsp, out=o5, lse=l5)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        p_ms = sum(e0.elapsed_time(e1) for e0, e1 in pev) / len(pev)
+        pbytes = decode_bytes(B5, Hq5, Hkv5, Nk5, d5) + B5 * (Nk5 // page) * 4  # + the block table
+        p_gbs = pbytes / (p_ms * 1e-3) / 1e9
+        paged = {"value": round(p_gbs, 1), "unit": "GB/s", "page_size": page,
+                 "workload": "split-KV decode B=64 Hq=32 Hkv=8 Nk=32768 d=128 S=16 bf16, 16-key pages in a "
+                             "shuffled pool",
+                 "algorithmic_bytes": pbytes, "avg_call_ms": round(p_ms, 5),
+                 "roofline": {"bound": "hbm", "achieved": round(p_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": round(p_gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+        del kp, vp
+
     fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
     split_ms = [e[1].elapsed_time(e[2]) for e in events]
     merge_ms = [e[2].elapsed_time(e[3]) for e in events]
@@ -280,6 +319,7 @@ def main():
                          "traffic": load_traffic("decode_splitkv_bf16_kernel+lse_merge_kernel")},
         },
         "backward": bwd,
+        "decode_paged": paged,
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -13,7 +13,7 @@ from . import _lib
 from ._lib import FAError, FA_DECODE_SPLIT_ALIGN, FA_MAX_SPLITS  # noqa: F401
 
 __all__ = ["fa_fwd", "fa_decode_splitkv", "fa_lse_merge", "fa_decode", "fa_decode_workspace_bytes",
-           "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_last_error", "FAError",
+           "fa_decode_paged", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_last_error", "FAError",
            "default_scale"]
 
 _DTYPES = {torch.bfloat16: _lib.FA_BF16, torch.float32: _lib.FA_F32}
@@ -173,6 +173,44 @@ def fa_decode(q, k_cache, v_cache, kv_seqlens=None, num_splits=16, scale=None, w
     _lib.check(lib.fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, Hq, Hkv, Nk, d,
                              s, _ptr(lens), num_splits, _ptr(workspace), workspace.numel(),
                              _DTYPES[q.dtype], _stream(q)))
+    return out, lse
+
+
+def fa_decode_paged(q, k_pages, v_pages, block_table, kv_seqlens, num_splits=16, scale=None, workspace=None,
+                    out=None, lse=None):
+    """Single-token decode over a paged KV cache (bf16).
+
+    q [B,Hq,1,d]; k_pages, v_pages [num_pages, Hkv, page_size, d]; block_table [B, max_pages] int32;
+    kv_seqlens [B] int32.  Returns (o [B,Hq,1,d], lse [B,Hq,1] float32).
+    """
+    _check_tensor(q, "q", torch.bfloat16, 4)
+    _check_tensor(k_pages, "k_pages", torch.bfloat16, 4, q.device)
+    _check_tensor(v_pages, "v_pages", torch.bfloat16, 4, q.device)
+    _check_tensor(block_table, "block_table", torch.int32, 2, q.device)
+    B, Hq, nq, d = q.shape
+    num_pages, Hkv, page_size = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if nq != 1 or tuple(v_pages.shape) != tuple(k_pages.shape) or k_pages.shape[3] != d:
+        raise ValueError("q must be [B,Hq,1,d] and k_pages/v_pages [num_pages,Hkv,page_size,d]")
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have B rows")
+    lens = _lens(kv_seqlens, B, q.device)
+    if lens is None:
+        raise ValueError("kv_seqlens is required for a paged cache")
+    lib = _lib.load()
+    need = int(lib.fa_decode_workspace_bytes(B, Hq, d, num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_tensor(workspace, "workspace", torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=q.device)
+    _check_tensor(out, "out", q.dtype, 4, q.device)
+    _check_tensor(lse, "lse", torch.float32, 3, q.device)
+    s = default_scale(d) if scale is None else float(scale)
+    _lib.check(lib.fa_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(out), _ptr(lse),
+                                   B, Hq, Hkv, num_pages, page_size, block_table.shape[1], d, s, _ptr(lens),
+                                   num_splits, _ptr(workspace), workspace.numel(), _lib.FA_BF16, _stream(q)))
     return out, lse
 
 

@@ -22,6 +22,7 @@ PROTOTYPES = {
     "fa_decode_splitkv": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _i, _i, _p]),
     "fa_lse_merge": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _p]),
     "fa_decode": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _i, _p, _sz, _i, _p]),
+    "fa_decode_paged": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _i, _p, _sz, _i, _p]),
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "fa_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _p, _sz, _i, _p]),
     "fa_status_string": (ctypes.c_char_p, [_i]),

@@ -199,6 +199,42 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, 
 }
 
 
+int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table, void* o,
+                    float* lse, int B, int Hq, int Hkv, int num_pages, int page_size, int max_pages_per_seq, int d,
+                    float scale, const int32_t* kv_seqlens, int num_splits, void* workspace,
+                    size_t workspace_bytes, int dtype, void* stream) {
+  if (page_size < 1 || max_pages_per_seq < 1 || num_pages < 1)
+    return fail(FA_ERR_INVALID_ARG, "page_size, max_pages_per_seq and num_pages must be >= 1 (got %d, %d, %d)",
+                page_size, max_pages_per_seq, num_pages);
+  if ((long long)page_size * max_pages_per_seq > (1LL << 24))
+    return fail(FA_ERR_UNSUPPORTED, "page_size * max_pages_per_seq exceeds 2^24 keys per sequence");
+  const int capacity = page_size * max_pages_per_seq;
+  int st = check_decode_args(q, k_pages, v_pages, B, Hq, Hkv, capacity, d, scale, num_splits, dtype);
+  if (st != FA_OK) return st;
+  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged supports bf16 only");
+  if ((long long)B * Hq == 0) return ok();
+  if ((st = check_ptr(block_table, 4, "block_table")) != FA_OK) return st;
+  if ((st = check_ptr(kv_seqlens, 4, "kv_seqlens")) != FA_OK) return st;
+  if ((st = check_ptr(o, 16, "o")) != FA_OK) return st;
+  if ((st = check_ptr(lse, 4, "lse")) != FA_OK) return st;
+  const size_t need = fa_decode_workspace_bytes(B, Hq, d, num_splits);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  const size_t rows = (size_t)B * Hq;
+  float* o_part = (float*)workspace;
+  float* lse_part = (float*)((char*)workspace + lse_offset(rows * num_splits * d * sizeof(float)));
+  fa::AttnArgs a = make_args(q, k_pages, v_pages, nullptr, nullptr, kv_seqlens, B, Hq, Hkv, 1, capacity, d, scale,
+                             0, stream);
+  fa::PartialOut part{o_part, lse_part, num_splits};
+  fa::PagedKV paged{block_table, page_size, max_pages_per_seq, num_pages};
+  hipError_t e = fa::launch_decode_splitkv_bf16(a, part, &paged);
+  if (e != hipSuccess) return hip_status(e, "fa_decode_paged split stage launch");
+  return hip_status(fa::launch_lse_merge(o_part, lse_part, o, lse, (int)rows, d, num_splits, true,
+                                         (hipStream_t)stream),
+                    "fa_decode_paged merge stage launch");
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq, int d) {
   if (B < 0 || Hq < 0 || Nq < 0 || (d != 64 && d != 128)) return 0;
   return ((size_t)B * Hq * Nq * sizeof(float) + 255) / 256 * 256;

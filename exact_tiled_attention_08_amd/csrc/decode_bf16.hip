@@ -42,9 +42,15 @@ struct DecParams {
   int group;      // Hq / Hkv
   int n_qblocks;  // ceil(group / 32)
   float scale_log2;
+  // paged cache only: pool [num_pages, Hkv, page_size, D], table [B, max_pages]
+  const int32_t* block_table;
+  int page_size, max_pages, num_pages;
+  float inv_page;  // 1 / page_size
 };
 
-template <int D>
+// PAGED: key j of sequence b is row j % page_size of page block_table[b][j / page_size]
+// (page indices clamped to the pool); otherwise the cache is contiguous BHSD.
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void decode_splitkv_bf16_kernel(DecParams p) {
   using T = DecTile<D>;
   constexpr int BN = T::BN;
@@ -89,6 +95,23 @@ __global__ __launch_bounds__(256) void decode_splitkv_bf16_kernel(DecParams p) {
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
 
   uint4 kreg[T::CHUNKS], vreg[T::CHUNKS];
+  // Paged cache: the page of each of this thread's rows, fetched two tiles
+  // ahead so that the table lookup does not add its latency to the K/V loads.
+  // key = page * page_size + rem, from a float reciprocal and a +-1 fix-up
+  // (exact for keys < 2^24, which the entry point guarantees).
+  int pgr[T::CHUNKS], rem[T::CHUNKS];
+  auto fetch_pages = [&](int t) {
+#pragma unroll
+    for (int c = 0; c < T::CHUNKS; ++c) {
+      const int key = ks + t * BN + (tid + c * T::THREADS) / T::DCH;
+      int qi = (int)((float)key * p.inv_page);
+      int r = key - qi * p.page_size;
+      if (r < 0) { --qi; r += p.page_size; }
+      if (r >= p.page_size) { ++qi; r -= p.page_size; }
+      rem[c] = r;
+      pgr[c] = key < ke ? p.block_table[(size_t)b * p.max_pages + qi] : 0;
+    }
+  };
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int c = 0; c < T::CHUNKS; ++c) {
@@ -96,7 +119,13 @@ __global__ __launch_bounds__(256) void decode_splitkv_bf16_kernel(DecParams p) {
       const int row = idx / T::DCH, col = idx % T::DCH;
       const int key = ks + t * BN + row;
       if (key < ke) {
-        const size_t off = (kv_base + key) * D + col * 8;
+        size_t off;
+        if (PAGED) {
+          const int pg = min(max(pgr[c], 0), p.num_pages - 1);
+          off = (((size_t)pg * p.Hkv + hk) * p.page_size + rem[c]) * D + col * 8;
+        } else {
+          off = (kv_base + key) * D + col * 8;
+        }
         kreg[c] = *(const uint4*)(p.k + off);
         vreg[c] = *(const uint4*)(p.v + off);
       } else {
@@ -119,12 +148,19 @@ __global__ __launch_bounds__(256) void decode_splitkv_bf16_kernel(DecParams p) {
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int kb = wave;  // this wave's 32-key block of every tile
 
-  if (n_t > 0) load_tile(0);
+  if (n_t > 0) {
+    if (PAGED) fetch_pages(0);
+    load_tile(0);
+    if (PAGED && n_t > 1) fetch_pages(1);
+  }
   for (int t = 0; t < n_t; ++t) {
     __syncthreads();
     store_tile();
     __syncthreads();
-    if (t + 1 < n_t) load_tile(t + 1);
+    if (t + 1 < n_t) {
+      load_tile(t + 1);
+      if (PAGED && t + 2 < n_t) fetch_pages(t + 2);
+    }
 
     f32x16 s = f32x16{};
     const uint16_t* kp = k_lds + (kb * 32 + li) * T::KSTRIDE + 8 * hi;
@@ -217,7 +253,7 @@ __global__ __launch_bounds__(256) void decode_splitkv_bf16_kernel(DecParams p) {
 }
 
 template <int D>
-static hipError_t launch_decode_t(const AttnArgs& a, const PartialOut& part) {
+static hipError_t launch_decode_t(const AttnArgs& a, const PartialOut& part, const PagedKV* paged) {
   DecParams p;
   p.q = (const uint16_t*)a.q;
   p.k = (const uint16_t*)a.k;
@@ -229,15 +265,23 @@ static hipError_t launch_decode_t(const AttnArgs& a, const PartialOut& part) {
   p.group = a.Hq / a.Hkv;
   p.n_qblocks = (p.group + 31) / 32;
   p.scale_log2 = a.scale * kLog2e;
+  p.block_table = paged ? paged->block_table : nullptr;
+  p.page_size = paged ? paged->page_size : 0;
+  p.max_pages = paged ? paged->max_pages : 0;
+  p.num_pages = paged ? paged->num_pages : 0;
+  p.inv_page = paged ? 1.0f / (float)paged->page_size : 0.f;
   const long long gy = (long long)a.Hkv * p.n_qblocks;
   if (gy > 65535 || a.B > 65535) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(decode_splitkv_bf16_kernel<D>, dim3(part.num_splits, (unsigned)gy, a.B), dim3(256), 0,
-                     a.stream, p);
+  const dim3 grid(part.num_splits, (unsigned)gy, a.B);
+  if (paged)
+    hipLaunchKernelGGL((decode_splitkv_bf16_kernel<D, true>), grid, dim3(256), 0, a.stream, p);
+  else
+    hipLaunchKernelGGL((decode_splitkv_bf16_kernel<D, false>), grid, dim3(256), 0, a.stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_splitkv_bf16(const AttnArgs& a, const PartialOut& part) {
-  return a.d == 128 ? launch_decode_t<128>(a, part) : launch_decode_t<64>(a, part);
+hipError_t launch_decode_splitkv_bf16(const AttnArgs& a, const PartialOut& part, const PagedKV* paged) {
+  return a.d == 128 ? launch_decode_t<128>(a, part, paged) : launch_decode_t<64>(a, part, paged);
 }
 
 // ---------------------------------------------------------------------------

@@ -31,8 +31,16 @@ hipError_t launch_fwd_bf16(const AttnArgs& a);
 // float32 forward; with part != nullptr it computes split-KV partials instead
 // of the final output (single-token decode in float32).
 hipError_t launch_fwd_f32(const AttnArgs& a, const PartialOut* part);
-// bf16 split-KV decode partials on matrix cores (Nq == 1).
-hipError_t launch_decode_splitkv_bf16(const AttnArgs& a, const PartialOut& part);
+// A paged KV cache: pools k, v [num_pages, Hkv, page_size, d] and a block
+// table [B, max_pages] of page indices in key order.
+struct PagedKV {
+  const int32_t* block_table;
+  int page_size, max_pages, num_pages;
+};
+
+// bf16 split-KV decode partials on matrix cores (Nq == 1); with paged != null
+// the cache is read through the block table (a.Nk = max_pages * page_size).
+hipError_t launch_decode_splitkv_bf16(const AttnArgs& a, const PartialOut& part, const PagedKV* paged = nullptr);
 // Exact log-sum-exp merge of split partials into o (bf16 or f32) and lse.
 hipError_t launch_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
                             int rows, int d, int num_splits, bool out_bf16, hipStream_t stream);

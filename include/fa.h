@@ -137,6 +137,28 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, 
               int num_splits, void* workspace, size_t workspace_bytes, int dtype, void* stream);
 
 /*
+ * fa_decode_paged -- fa_decode over a paged KV cache.  The pages place the KV
+ * cache under page management (PagedAttention) without fixing a layout
+ * (Concept note, section "是什么", table of related concepts; Explainer,
+ * "paged" variants).  Here the cache is a pool of pages:
+ *   k_pages, v_pages [num_pages, Hkv, page_size, d] bf16 in;
+ *   block_table [B, max_pages_per_seq] int32 in (DEVICE): sequence b's pages
+ *   in key order, so key j of sequence b is row j % page_size of page
+ *   block_table[b][j / page_size];
+ *   kv_seqlens [B] int32 in (DEVICE, required): valid keys per sequence,
+ *   clamped to [0, page_size * max_pages_per_seq].
+ * Table entries are clamped to [0, num_pages) on the device (they cannot be
+ * checked without a sync); entries past a sequence's length are never read.
+ * q, o, lse, num_splits, workspace (fa_decode_workspace_bytes) and scale are
+ * as for fa_decode.  Only dtype FA_BF16 is supported, and a sequence holds at
+ * most 2^24 keys (page_size * max_pages_per_seq <= 2^24).
+ */
+int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                    void* o, float* lse, int B, int Hq, int Hkv, int num_pages, int page_size,
+                    int max_pages_per_seq, int d, float scale, const int32_t* kv_seqlens, int num_splits,
+                    void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
  * fa_bwd_workspace_bytes -- bytes of device workspace fa_bwd needs: one
  * float32 per query row, [B, Hq, Nq] (rowsum(dO * O)).  Returns 0 for
  * invalid arguments.

@@ -151,3 +151,21 @@ def test_bwd_empty_is_noop(lib):
                ws=None) == _lib.FA_OK
     assert bwd(lib, Hq=0, Hkv=0, q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None,
                ws=None) == _lib.FA_OK
+
+
+def paged(lib, q=P, kp=P, vp=P, table=P, o=P, lse=P, B=2, Hq=8, Hkv=2, num_pages=10, page=16, max_pages=4,
+          d=128, scale=0.1, lens=P, S=4, ws=P, ws_bytes=None, dtype=1):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_decode_workspace_bytes(B, Hq, d, S) if S >= 1 else 0
+    return lib.fa_decode_paged(q, kp, vp, table, o, lse, B, Hq, Hkv, num_pages, page, max_pages, d, scale, lens,
+                               S, ws, ws_bytes, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(page=0), BAD), (dict(max_pages=0), BAD), (dict(num_pages=0), BAD), (dict(table=None), BAD),
+    (dict(lens=None), BAD), (dict(table=P + 2), BAD), (dict(dtype=0), UNSUP), (dict(ws=None), WS),
+    (dict(d=96), UNSUP), (dict(S=0), UNSUP), (dict(kp=None), BAD), (dict(o=None), BAD),
+    (dict(page=1 << 20, max_pages=1 << 12), UNSUP),
+])
+def test_paged_rejects(lib, kwargs, status):
+    assert paged(lib, **kwargs) == status
