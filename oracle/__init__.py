@@ -14,6 +14,7 @@ from .attention import (  # noqa: F401
     attention_ref,
     attention_probs_ref,
     attention_bwd_ref,
+    attention_varlen_ref,
     online_softmax_blocked,
     merge_partials,
     split_bounds,

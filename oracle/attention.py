@@ -308,6 +308,64 @@ def decode_partials_ref(q, k, v, kv_seqlens, scale, num_splits, tile):
     return O, LSE
 
 
+def _seq_bounds(cu, b, total):
+    """Rows [start, stop) of packed sequence b; offsets are clamped to [0, total]."""
+    start = int(min(max(int(cu[b]), 0), total))
+    stop = int(min(max(int(cu[b + 1]), start), total))
+    return start, stop
+
+
+def attention_varlen_ref(q, k, v, cu_seqlens_q, cu_seqlens_k, causal=False, scale=None):
+    """Exact attention over packed variable-length sequences, fp64.
+
+    The pages put padding masks inside the tile (Concept note, section "是什么")
+    and contrast prompt processing with one-token decode against a KV cache
+    (the same note's list of misconceptions); they give no packed layout.  The
+    plainest reading, used here: the sequences of a batch are concatenated
+    along the token axis of every head, q [Hq, total_q, d] and k, v
+    [Hkv, total_k, d]; sequence b owns query rows cu_seqlens_q[b] ..
+    cu_seqlens_q[b+1] - 1 and key rows cu_seqlens_k[b] .. cu_seqlens_k[b+1] - 1,
+    and attends only to its own keys.  Each sequence is the definition above
+    with Nq = Lq_b and Nk = Lk_b, so the causal mask is bottom-right aligned
+    per sequence: local key j is visible to local query i iff j <= i + Lk_b - Lq_b
+    (a chunk of new queries sees the whole cache before it).  A query row with
+    no visible key has O = 0, LSE = -inf.  Returns O [Hq, total_q, d] and
+    LSE [Hq, total_q]; rows outside every sequence stay NaN.
+    """
+    q = to_f64(q); k = to_f64(k); v = to_f64(v)
+    if q.ndim != 3 or k.ndim != 3 or v.ndim != 3 or k.shape != v.shape or k.shape[2] != q.shape[2]:
+        raise ValueError("q must be [Hq, total_q, d]; k, v [Hkv, total_k, d]")
+    Hq, total_q, d = q.shape
+    Hkv, total_k = k.shape[0], k.shape[1]
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    cu_q = np.asarray(to_f64(cu_seqlens_q), dtype=np.int64)
+    cu_k = np.asarray(to_f64(cu_seqlens_k), dtype=np.int64)
+    if cu_q.shape != cu_k.shape or cu_q.ndim != 1 or cu_q.size < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be int[B + 1]")
+    if scale is None:
+        scale = default_scale(d)
+    scale = float(np.float32(scale))
+    O = np.full((Hq, total_q, d), np.nan)
+    LSE = np.full((Hq, total_q), np.nan)
+    for b in range(cu_q.size - 1):
+        qs, qe = _seq_bounds(cu_q, b, total_q)
+        ks, ke = _seq_bounds(cu_k, b, total_k)
+        if qe == qs:
+            continue
+        if ke == ks:  # no keys at all: every row is empty
+            O[:, qs:qe] = 0.0
+            LSE[:, qs:qe] = -np.inf
+            continue
+        allowed = _allowed(qe - qs, ke - ks, ke - ks, causal)
+        for hq in range(Hq):
+            hk = _head_map(hq, Hq, Hkv)
+            o, lse, _ = _one_head(q[hq, qs:qe], k[hk, ks:ke], v[hk, ks:ke], allowed, scale)
+            O[hq, qs:qe] = o
+            LSE[hq, qs:qe] = lse
+    return O, LSE
+
+
 def paged_to_contiguous(pages, block_table, lengths, page_size):
     """Gather a paged KV cache into contiguous per-sequence rows.
 

@@ -294,11 +294,93 @@ def check_paged_gather():
     assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
 
 
+def _varlen_brute(q, k, v, cu_q, cu_k, causal, scale):
+    """Attention over the packed token axis, one (query token, key token) pair
+    at a time: a pair takes part iff both tokens belong to the same sequence
+    and, under the causal mask, the key's position counted from the end of its
+    sequence is at least the query's (bottom-right alignment)."""
+    Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[0], k.shape[1]
+    B = len(cu_q) - 1
+    O = np.full((Hq, Tq, d), np.nan)
+    L = np.full((Hq, Tq), np.nan)
+    for h in range(Hq):
+        hk = h * Hkv // Hq
+        for t in range(Tq):
+            b = next(bb for bb in range(B) if cu_q[bb] <= t < cu_q[bb + 1])
+            from_end_q = cu_q[b + 1] - 1 - t
+            scores, rows = [], []
+            for u in range(Tk):
+                if not cu_k[b] <= u < cu_k[b + 1]:
+                    continue
+                if causal and cu_k[b + 1] - 1 - u < from_end_q:
+                    continue
+                scores.append(scale * sum(q[h, t, c] * k[hk, u, c] for c in range(d)))
+                rows.append(u)
+            if not scores:
+                O[h, t], L[h, t] = 0.0, -math.inf
+                continue
+            mx = max(scores)
+            w = [math.exp(x - mx) for x in scores]
+            tot = sum(w)
+            O[h, t] = sum(wi * v[hk, u] for wi, u in zip(w, rows)) / tot
+            L[h, t] = mx + math.log(tot)
+    return O, L
+
+
+def check_varlen_brute_force():
+    rng = np.random.default_rng(11)
+    lq, lk = [3, 0, 5, 2, 4, 3], [6, 2, 5, 0, 3, 1]  # empty query / key sets, Lq > Lk, Lq < Lk
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    Hq, Hkv, d = 4, 2, 5
+    q, k, v = rng.standard_normal((Hq, cu_q[-1], d)), rng.standard_normal((Hkv, cu_k[-1], d)), \
+        rng.standard_normal((Hkv, cu_k[-1], d))
+    for causal in (False, True):
+        O, L = oracle.attention_varlen_ref(q, k, v, cu_q, cu_k, causal=causal, scale=0.7)
+        Ob, Lb = _varlen_brute(q, k, v, cu_q, cu_k, causal, float(np.float32(0.7)))
+        assert np.allclose(O, Ob, atol=1e-12, rtol=0) and np.array_equal(np.isinf(L), np.isinf(Lb))
+        fin = np.isfinite(Lb)
+        assert np.allclose(L[fin], Lb[fin], atol=1e-12, rtol=0)
+
+
+def check_varlen_chunked_prefill():
+    # one causal sequence of 23 tokens, its queries taken in chunks [0,7), [7,16),
+    # [16,23) against the keys up to the end of each chunk, equals the rows of
+    # the one-shot causal attention
+    rng = np.random.default_rng(12)
+    H, L, d = 3, 23, 6
+    q, k, v = rng.standard_normal((1, H, L, d)), rng.standard_normal((1, H, L, d)), rng.standard_normal((1, H, L, d))
+    O_full, L_full = oracle.attention_ref(q, k, v, causal=True, scale=0.4)
+    ends = [7, 16, 23]
+    kp = np.concatenate([k[0, :, :e] for e in ends], axis=1)
+    vp = np.concatenate([v[0, :, :e] for e in ends], axis=1)
+    cu_q = np.array([0] + ends)
+    cu_k = np.concatenate([[0], np.cumsum(ends)])
+    O, LSE = oracle.attention_varlen_ref(q[0], kp, vp, cu_q, cu_k, causal=True, scale=0.4)
+    assert np.allclose(O, O_full[0], atol=1e-12, rtol=0) and np.allclose(LSE, L_full[0], atol=1e-12, rtol=0)
+
+
+def check_varlen_equal_lengths():
+    # sequences of equal lengths packed along the token axis equal the batched layout
+    rng = np.random.default_rng(13)
+    B, Hq, Hkv, nq, nk, d = 3, 4, 2, 5, 8, 4
+    q, k, v = rng.standard_normal((B, Hq, nq, d)), rng.standard_normal((B, Hkv, nk, d)), \
+        rng.standard_normal((B, Hkv, nk, d))
+    for causal in (False, True):
+        O_b, L_b = oracle.attention_ref(q, k, v, causal=causal)
+        pack = lambda x: np.concatenate(list(x), axis=1)  # [B, H, N, d] -> [H, B*N, d]
+        O, LSE = oracle.attention_varlen_ref(pack(q), pack(k), pack(v), np.arange(B + 1) * nq,
+                                             np.arange(B + 1) * nk, causal=causal)
+        assert np.allclose(O, pack(O_b), atol=1e-12, rtol=0)
+        assert np.allclose(LSE, np.concatenate(list(L_b), axis=1), atol=1e-12, rtol=0)
+
+
 PIN_CHECKS = [check_rows_sum_to_one, check_constant_v, check_single_key, check_causal_row0,
               check_zero_q_closed_form, check_two_keys, check_blocked_recurrence,
               check_key_permutation, check_gqa_equals_mha, check_against_torch_sdpa,
               check_merge_identity, check_split_bounds, check_bwd_finite_differences,
-              check_bwd_against_autograd, check_bwd_invariants, check_paged_gather]
+              check_bwd_against_autograd, check_bwd_invariants, check_paged_gather,
+              check_varlen_brute_force, check_varlen_chunked_prefill, check_varlen_equal_lengths]
 
 
 @pytest.mark.parametrize("check", PIN_CHECKS, ids=lambda f: f.__name__)
@@ -416,6 +498,39 @@ def _mut_paged_row_reversed(pages, block_table, lengths, page_size):
     return out
 
 
+def _varlen_variant(q, k, v, cu_q, cu_k, causal, scale, top_left=False, keys_at_q_offsets=False):
+    q = A.to_f64(q); k = A.to_f64(k); v = A.to_f64(v)
+    Hq, Tq, d = q.shape
+    Hkv = k.shape[0]
+    scale = float(np.float32(scale if scale is not None else A.default_scale(d)))
+    O, L = np.full((Hq, Tq, d), np.nan), np.full((Hq, Tq), np.nan)
+    cu_q, cu_k = np.asarray(cu_q), np.asarray(cu_k)
+    for b in range(len(cu_q) - 1):
+        qs, qe = int(cu_q[b]), int(cu_q[b + 1])
+        ks, ke = (qs, qs + int(cu_k[b + 1] - cu_k[b])) if keys_at_q_offsets else (int(cu_k[b]), int(cu_k[b + 1]))
+        if qe == qs:
+            continue
+        if ke == ks:
+            O[:, qs:qe], L[:, qs:qe] = 0.0, -np.inf
+            continue
+        i = np.arange(qe - qs)[:, None]; j = np.arange(ke - ks)[None, :]
+        allowed = np.ones((qe - qs, ke - ks), dtype=bool)
+        if causal:
+            allowed = j <= i if top_left else j <= i + (ke - ks) - (qe - qs)
+        for hq in range(Hq):
+            hk = A._head_map(hq, Hq, Hkv)
+            O[hq, qs:qe], L[hq, qs:qe], _ = A._one_head(q[hq, qs:qe], k[hk, ks:ke], v[hk, ks:ke], allowed, scale)
+    return O, L
+
+
+def _mut_varlen_top_left(q, k, v, cu_q, cu_k, causal=False, scale=None):
+    return _varlen_variant(q, k, v, cu_q, cu_k, causal, scale, top_left=True)
+
+
+def _mut_varlen_keys_at_q_offsets(q, k, v, cu_q, cu_k, causal=False, scale=None):
+    return _varlen_variant(q, k, v, cu_q, cu_k, causal, scale, keys_at_q_offsets=True)
+
+
 _ORIG_PAGED = A.paged_to_contiguous
 _ORIG_ONE_HEAD = A._one_head
 _ORIG_MERGE = A.merge_partials
@@ -425,13 +540,15 @@ MUTANTS = [("_allowed", _mut_causal_off_by_one), ("_allowed", _mut_padding_inclu
            ("_one_head", _mut_scale_twice), ("_one_head", _mut_transposed_probs),
            ("merge_partials", _mut_merge_unweighted), ("attention_bwd_ref", _mut_bwd_no_rowsum),
            ("attention_bwd_ref", _mut_bwd_unscaled_dq), ("attention_bwd_ref", _mut_bwd_gqa_overwrite),
-           ("paged_to_contiguous", _mut_paged_row_reversed)]
+           ("paged_to_contiguous", _mut_paged_row_reversed),
+           ("attention_varlen_ref", _mut_varlen_top_left),
+           ("attention_varlen_ref", _mut_varlen_keys_at_q_offsets)]
 
 
 @pytest.mark.parametrize("name,mutant", MUTANTS, ids=lambda x: getattr(x, "__name__", x))
 def test_pins_catch_planted_mistake(monkeypatch, name, mutant):
     monkeypatch.setattr(A, name, mutant)
-    if name in ("merge_partials", "attention_bwd_ref", "paged_to_contiguous"):
+    if name in ("merge_partials", "attention_bwd_ref", "paged_to_contiguous", "attention_varlen_ref"):
         monkeypatch.setattr(oracle, name, mutant)
     failed = []
     for check in PIN_CHECKS:
