@@ -126,6 +126,8 @@ def main():
     ap.add_argument("--bwd-steps", type=int, default=20, help="timed backward calls (0 = skip the backward)")
     ap.add_argument("--paged-steps", type=int, default=20,
                     help="timed paged-cache decode calls (0 = skip the paged decode)")
+    ap.add_argument("--varlen-steps", type=int, default=20,
+                    help="timed packed variable-length and chunked prefill calls (0 = skip them)")
     ap.add_argument("--only", choices=["prefill", "decode", "backward", "copy"], default=None,
                     help="profiling aid: run only one part of the step (or a 1 GiB device copy used to "
                          "calibrate the HBM byte counters) and print no JSON")
@@ -264,6 +266,42 @@ def main():
                               "frac": round(p_gbs / PEAK_HBM_GBS, 4), "traffic": None}}
         del kp, vp
 
+    varlen = None
+    if args.varlen_steps > 0:
+        varlen = {}
+        # Packed sequences with the GQA workload's length mix (U{2048..4096},
+        # the same draw as its padding lengths): Hq=32, Hkv=8, d=128, causal.
+        # "packed": each sequence attends to itself; "chunked": a chunk of its
+        # last 512 tokens against all of its keys (the rest is the KV cache).
+        lens = inputs.lengths(4, 4, 2048, 4096).tolist()
+        chunk = 512
+        for name, lq in (("packed", lens), ("chunked", [chunk] * len(lens))):
+            qv, kv_, vv, cq, ck = inputs.make_packed(4, lq, lens, 32, 8, 128)
+            qv, kv_, vv, cq, ck = (t.to(dev) for t in (qv, kv_, vv, cq, ck))
+            ov = torch.empty_like(qv)
+            lv = torch.empty(qv.shape[:2], dtype=torch.float32, device=dev)
+            mq = max(lq)
+            for _ in range(10):
+                fa.fa_fwd_varlen(qv, kv_, vv, cq, ck, mq, causal=True, out=ov, lse=lv)
+            vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.varlen_steps)]
+            torch.cuda.synchronize()
+            for e0, e1 in vev:
+                e0.record(stream)
+                fa.fa_fwd_varlen(qv, kv_, vv, cq, ck, mq, causal=True, out=ov, lse=lv)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            v_ms = sum(e0.elapsed_time(e1) for e0, e1 in vev) / len(vev)
+            v_flop = sum(prefill_flops(1, 32, a, b, 128, True) for a, b in zip(lq, lens))
+            v_tf = v_flop / (v_ms * 1e-3) / 1e12
+            varlen[name] = {
+                "value": round(v_tf, 2), "unit": "TFLOP/s", "avg_call_ms": round(v_ms, 5), "flop_per_call": v_flop,
+                "workload": f"fa_fwd_varlen Hq=32 Hkv=8 d=128 causal bf16, key lengths {lens}, query lengths {lq}",
+                "roofline": {"bound": "mfma", "achieved": round(v_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(v_tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+            print(f"[bench] varlen {name}: {v_ms:.3f} ms, {v_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+            del qv, kv_, vv, ov, lv
+
     fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
     split_ms = [e[1].elapsed_time(e[2]) for e in events]
     merge_ms = [e[2].elapsed_time(e[3]) for e in events]
@@ -320,6 +358,7 @@ def main():
         },
         "backward": bwd,
         "decode_paged": paged,
+        "prefill_varlen": varlen,
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -1,4 +1,5 @@
-"""Exact tiled attention (prefill forward and backward, split-KV decode, LSE merge) on gfx950.
+"""Exact tiled attention (prefill forward -- dense, padded or packed variable-length -- and
+backward, split-KV decode over contiguous or paged caches, LSE merge) on gfx950.
 
 Thin torch-facing wrappers over the C ABI in include/fa.h.  Each function has
 the name of the C entry point it marshals arguments for; all computation runs
@@ -12,7 +13,7 @@ import torch
 from . import _lib
 from ._lib import FAError, FA_DECODE_SPLIT_ALIGN, FA_MAX_SPLITS  # noqa: F401
 
-__all__ = ["fa_fwd", "fa_decode_splitkv", "fa_lse_merge", "fa_decode", "fa_decode_workspace_bytes",
+__all__ = ["fa_fwd", "fa_fwd_varlen", "fa_decode_splitkv", "fa_lse_merge", "fa_decode", "fa_decode_workspace_bytes",
            "fa_decode_paged", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_last_error", "FAError",
            "default_scale"]
 
@@ -82,6 +83,45 @@ def fa_fwd(q, k, v, causal=False, kv_seqlens=None, scale=None, out=None, lse=Non
     lib = _lib.load()
     _lib.check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, s,
                           int(bool(causal)), _ptr(lens), _DTYPES[q.dtype], _stream(q)))
+    return out, lse
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=False, scale=None, out=None,
+                  lse=None):
+    """Exact attention over packed variable-length sequences.
+
+    q [Hq, total_q, d], k/v [Hkv, total_k, d] (bf16 or f32); cu_seqlens_q and
+    cu_seqlens_k are int32 GPU tensors of B + 1 cumulative offsets;
+    max_seqlen_q (a host int) is at least the longest query sequence.
+    Returns (o [Hq, total_q, d] in q's dtype, lse [Hq, total_q] float32).
+    """
+    _check_tensor(q, "q", ndim=3)
+    if q.dtype not in _DTYPES:
+        raise ValueError("q must be bfloat16 or float32")
+    _check_tensor(k, "k", q.dtype, 3, q.device)
+    _check_tensor(v, "v", q.dtype, 3, q.device)
+    Hq, total_q, d = q.shape
+    Hkv, total_k = k.shape[0], k.shape[1]
+    if tuple(k.shape) != (Hkv, total_k, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [Hkv, total_k, d] matching q")
+    _check_tensor(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, q.device)
+    _check_tensor(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1, q.device)
+    if cu_seqlens_q.numel() < 1 or cu_seqlens_k.numel() != cu_seqlens_q.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 offsets")
+    B = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    _check_tensor(out, "out", q.dtype, 3, q.device)
+    _check_tensor(lse, "lse", torch.float32, 2, q.device)
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (Hq, total_q):
+        raise ValueError("out/lse have the wrong shape")
+    s = default_scale(d) if scale is None else float(scale)
+    lib = _lib.load()
+    _lib.check(lib.fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                                 _ptr(cu_seqlens_k), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), d, s,
+                                 int(bool(causal)), _DTYPES[q.dtype], _stream(q)))
     return out, lse
 
 

@@ -18,6 +18,7 @@ _p, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 # name -> (restype, argtypes); mirrors include/fa.h
 PROTOTYPES = {
     "fa_fwd": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _i, _p]),
+    "fa_fwd_varlen": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _p]),
     "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "fa_decode_splitkv": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _i, _i, _p]),
     "fa_lse_merge": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _p]),

@@ -131,6 +131,34 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return hip_status(fa::launch_fwd_f32(a, nullptr), "fa_fwd (f32) launch");
 }
 
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens_q,
+                  const int32_t* cu_seqlens_k, int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                  int d, float scale, int causal, int dtype, void* stream) {
+  int st = check_common(B, Hq, Hkv, total_q, total_k, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (max_seqlen_q < 0) return fail(FA_ERR_INVALID_ARG, "max_seqlen_q must be non-negative");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if ((long long)B * Hq * total_q == 0 || max_seqlen_q == 0) return ok();  // nothing to write
+  if ((st = check_ptr(cu_seqlens_q, 4, "cu_seqlens_q")) != FA_OK) return st;
+  if ((st = check_ptr(cu_seqlens_k, 4, "cu_seqlens_k")) != FA_OK) return st;
+  if ((st = check_ptr(q, 16, "q")) != FA_OK) return st;
+  if ((st = check_ptr(o, 16, "o")) != FA_OK) return st;
+  if ((st = check_ptr(lse, 4, "lse")) != FA_OK) return st;
+  if (total_k > 0) {
+    if ((st = check_ptr(k, 16, "k")) != FA_OK) return st;
+    if ((st = check_ptr(v, 16, "v")) != FA_OK) return st;
+  }
+  const long long tiles = ((long long)max_seqlen_q + 127) / 128 * B * Hq;
+  if (tiles > 0x7fffffffLL) return fail(FA_ERR_UNSUPPORTED, "problem too large for one launch");
+  fa::AttnArgs a = make_args(q, k, v, o, lse, nullptr, B, Hq, Hkv, max_seqlen_q, 0, d, scale, causal, stream);
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  if (dtype == FA_BF16) return hip_status(fa::launch_fwd_bf16(a), "fa_fwd_varlen (bf16) launch");
+  return hip_status(fa::launch_fwd_f32(a, nullptr), "fa_fwd_varlen (f32) launch");
+}
+
 size_t fa_decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
   if (B < 0 || Hq < 0 || (d != 64 && d != 128) || num_splits < 1 || num_splits > FA_MAX_SPLITS) return 0;
   const size_t rows = (size_t)B * Hq * num_splits;

@@ -169,6 +169,17 @@ __device__ __forceinline__ float pair_sum32(float x) {
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
+// Packed variable-length sequences: sequence b owns rows cu[b] .. cu[b+1]-1
+// of a [.., total, d] tensor.  Returns (first row, row count), with the
+// offsets clamped to [0, total] and a decreasing pair read as empty, so that
+// no row outside the tensor is ever addressed.
+__device__ __forceinline__ int2 packed_rows(const int32_t* cu, int b, int total) {
+  int s = cu[b], e = cu[b + 1];
+  s = s < 0 ? 0 : (s > total ? total : s);
+  e = e < s ? s : (e > total ? total : e);
+  return make_int2(s, e - s);
+}
+
 __device__ __forceinline__ int clamp_len(const int32_t* lens, int b, int nk) {
   if (lens == nullptr) return nk;
   int L = lens[b];

@@ -18,6 +18,13 @@ struct AttnArgs {
   float scale;
   int causal;
   hipStream_t stream;
+  // Packed variable-length sequences (cu_q == nullptr: the [B, H, N, d]
+  // layout).  q, o [Hq, total_q, d]; k, v [Hkv, total_k, d]; lse [Hq, total_q];
+  // sequence b owns query rows cu_q[b] .. cu_q[b+1]-1 and key rows
+  // cu_k[b] .. cu_k[b+1]-1.  Nq then bounds the longest query sequence.
+  const int32_t* cu_q = nullptr;
+  const int32_t* cu_k = nullptr;
+  int total_q = 0, total_k = 0;
 };
 
 struct PartialOut {

@@ -49,12 +49,48 @@ struct FwdParams {
   uint16_t* o;
   float* lse;
   const int32_t* kv_seqlens;
+  const int32_t* cu_q;  // packed layout only
+  const int32_t* cu_k;
+  int total_q, total_k;
   int B, Hq, Hkv, Nq, Nk;
   int n_qtiles;
   float scale_log2;  // scale * log2(e)
 };
 
-template <int D, bool CAUSAL, bool PADDED>
+// Sequence layouts: dense [B, H, N, d]; the same with per-sequence valid key
+// lengths; or packed variable-length sequences (rows of every head
+// concatenated along the token axis, [H, total, d], delimited by cumulative
+// offsets).
+enum SeqMode : int { kDense = 0, kPadded = 1, kPacked = 2 };
+
+// One (sequence, query head) of a forward call: the row index of its first
+// query and of its KV head's first key (rows of d elements; the LSE shares
+// the query index), its query and key counts, and the keys that may be seen.
+struct SeqRows {
+  size_t q_row0, kv_row0;
+  int nq, nk, kv_len;
+};
+
+template <int MODE>
+__device__ __forceinline__ SeqRows seq_rows(const FwdParams& p, int b, int hq, int hk) {
+  SeqRows r;
+  if constexpr (MODE == kPacked) {
+    const int2 qr = packed_rows(p.cu_q, b, p.total_q), kr = packed_rows(p.cu_k, b, p.total_k);
+    r.q_row0 = (size_t)hq * p.total_q + qr.x;
+    r.kv_row0 = (size_t)hk * p.total_k + kr.x;
+    r.nq = qr.y;
+    r.nk = r.kv_len = kr.y;
+  } else {
+    r.q_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
+    r.kv_row0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Nk;
+    r.nq = p.Nq;
+    r.nk = p.Nk;
+    r.kv_len = MODE == kPadded ? clamp_len(p.kv_seqlens, b, p.Nk) : p.Nk;
+  }
+  return r;
+}
+
+template <int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdParams p) {
   using T = FwdTile<D>;
   constexpr int BM = T::BM, BN = T::BN;
@@ -77,26 +113,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   const int b = bh / p.Hq, hq = bh - b * p.Hq;
   const int hk = hq / (p.Hq / p.Hkv);
 
-  const int kv_len = PADDED ? clamp_len(p.kv_seqlens, b, p.Nk) : p.Nk;
+  const SeqRows sr = seq_rows<MODE>(p, b, hq, hk);
+  const int nq = sr.nq, kv_len = sr.kv_len;
   const int q0 = qt * BM;
-  const int diag = p.Nk - p.Nq;  // key j visible to row i iff j <= i + diag
+  if (q0 >= nq) return;  // a packed sequence shorter than the longest one
+  const int diag = sr.nk - nq;  // key j visible to row i iff j <= i + diag
   int kend = kv_len;
   if (CAUSAL) {
-    const int q_last = min(q0 + BM, p.Nq) - 1;
+    const int q_last = min(q0 + BM, nq) - 1;
     kend = min(kend, q_last + diag + 1);
   }
   const int n_kt = kend > 0 ? (kend + BN - 1) / BN : 0;
 
-  const size_t q_base = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
-  const size_t kv_base = ((size_t)b * p.Hkv + hk) * (size_t)p.Nk;
-  const uint16_t* kg = p.k + kv_base * D;
-  const uint16_t* vg = p.v + kv_base * D;
+  const size_t q_base = sr.q_row0;
+  const uint16_t* kg = p.k + sr.kv_row0 * D;
+  const uint16_t* vg = p.v + sr.kv_row0 * D;
 
   // Q^T fragment: lane (li, hi) holds row q0 + 32*wave + li, columns
   // 16*s + 8*hi .. +7 for each k-step s.
   const int qrow = q0 + wave * 32 + li;
   bf16x8 qf[D / 16];
-  if (qrow < p.Nq) {
+  if (qrow < nq) {
     const uint16_t* qp = p.q + (q_base + qrow) * D + 8 * hi;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qf[s] = *(const bf16x8*)(qp + 16 * s);
@@ -261,7 +298,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   // ever written to memory.
   const float lt = pair_sum32(l);
   const float lrt = pair_sum32(lr);
-  if (qrow < p.Nq) {
+  if (qrow < nq) {
     const float inv = lt > 0.f ? 1.f / lrt : 0.f;
     uint16_t* op = p.o + (q_base + qrow) * D;
 #pragma unroll
@@ -298,7 +335,7 @@ struct PPTile {
   static constexpr int COPIES = BN / RPI / WAVES;     // 1 KiB copies per wave per tile (= 2)
 };
 
-template <bool CAUSAL, bool PADDED>
+template <bool CAUSAL, int MODE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_pp_kernel(FwdParams p) {
   using T = PPTile;
   constexpr int D = T::D, BM = T::BM, BN = T::BN;
@@ -317,26 +354,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int b = bh / p.Hq, hq = bh - b * p.Hq;
   const int hk = hq / (p.Hq / p.Hkv);
 
-  const int kv_len = PADDED ? clamp_len(p.kv_seqlens, b, p.Nk) : p.Nk;
+  const SeqRows sr = seq_rows<MODE>(p, b, hq, hk);
+  const int nq = sr.nq, kv_len = sr.kv_len;
   const int q0 = qt * BM;
-  const int diag = p.Nk - p.Nq;
+  if (q0 >= nq) return;  // a packed sequence shorter than the longest one
+  const int diag = sr.nk - nq;
   int kend = kv_len;
-  if (CAUSAL) kend = min(kend, min(q0 + BM, p.Nq) - 1 + diag + 1);
+  if (CAUSAL) kend = min(kend, min(q0 + BM, nq) - 1 + diag + 1);
   const int n_kt = kend > 0 ? (kend + BN - 1) / BN : 0;
   // tiles this wave's rows can see at all (later tiles are skipped, not masked)
   const int w_first = q0 + wave_u * 32;
   int w_kend = kv_len;
-  if (CAUSAL) w_kend = min(w_kend, min(w_first + 32, p.Nq) - 1 + diag + 1);
+  if (CAUSAL) w_kend = min(w_kend, min(w_first + 32, nq) - 1 + diag + 1);
   const int w_nkt = w_kend > 0 ? (w_kend + BN - 1) / BN : 0;
 
-  const size_t q_base = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
-  const size_t kv_base = ((size_t)b * p.Hkv + hk) * (size_t)p.Nk;
-  const uint16_t* kg = p.k + kv_base * D;
-  const uint16_t* vg = p.v + kv_base * D;
+  const size_t q_base = sr.q_row0;
+  const uint16_t* kg = p.k + sr.kv_row0 * D;
+  const uint16_t* vg = p.v + sr.kv_row0 * D;
 
   const int qrow = w_first + li;
   bf16x8 qf[D / 16];
-  if (qrow < p.Nq) {
+  if (qrow < nq) {
     const uint16_t* qp = p.q + (q_base + qrow) * D + 8 * hi;
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) qf[st] = *(const bf16x8*)(qp + 16 * st);
@@ -568,7 +606,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const float lt = pair_sum32(l);
   const float lrt = pair_sum32(lr);
-  if (qrow < p.Nq) {
+  if (qrow < nq) {
     const float inv = lt > 0.f ? 1.f / lrt : 0.f;
     uint16_t* op = p.o + (q_base + qrow) * D;
 #pragma unroll
@@ -584,8 +622,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-template <bool CAUSAL, bool PADDED>
-static hipError_t launch_fwd_bf16_pp(const AttnArgs& a) {
+static FwdParams make_params(const AttnArgs& a, int bm) {
   FwdParams p;
   p.q = (const uint16_t*)a.q;
   p.k = (const uint16_t*)a.k;
@@ -593,44 +630,46 @@ static hipError_t launch_fwd_bf16_pp(const AttnArgs& a) {
   p.o = (uint16_t*)a.o;
   p.lse = a.lse;
   p.kv_seqlens = a.kv_seqlens;
+  p.cu_q = a.cu_q;
+  p.cu_k = a.cu_k;
+  p.total_q = a.total_q;
+  p.total_k = a.total_k;
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
-  p.n_qtiles = (a.Nq + PPTile::BM - 1) / PPTile::BM;
+  p.n_qtiles = (a.Nq + bm - 1) / bm;
   p.scale_log2 = a.scale * kLog2e;
+  return p;
+}
+
+template <bool CAUSAL, int MODE>
+static hipError_t launch_fwd_bf16_pp(const AttnArgs& a) {
+  const FwdParams p = make_params(a, PPTile::BM);
   const long long grid = (long long)p.n_qtiles * a.B * a.Hq;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_pp_kernel<CAUSAL, PADDED>), dim3((unsigned)grid), dim3(PPTile::THREADS), 0,
+  hipLaunchKernelGGL((fwd_bf16_pp_kernel<CAUSAL, MODE>), dim3((unsigned)grid), dim3(PPTile::THREADS), 0,
                      a.stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool PADDED>
+template <int D, bool CAUSAL, int MODE>
 static hipError_t launch_fwd_bf16_t(const AttnArgs& a) {
   using T = FwdTile<D>;
-  FwdParams p;
-  p.q = (const uint16_t*)a.q;
-  p.k = (const uint16_t*)a.k;
-  p.v = (const uint16_t*)a.v;
-  p.o = (uint16_t*)a.o;
-  p.lse = a.lse;
-  p.kv_seqlens = a.kv_seqlens;
-  p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
-  p.n_qtiles = (a.Nq + T::BM - 1) / T::BM;
-  p.scale_log2 = a.scale * kLog2e;
+  const FwdParams p = make_params(a, T::BM);
   const long long grid = (long long)p.n_qtiles * a.B * a.Hq;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, PADDED>), dim3((unsigned)grid), dim3(T::THREADS), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, MODE>), dim3((unsigned)grid), dim3(T::THREADS), 0,
                      a.stream, p);
   return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_mode(const AttnArgs& a) {
+  if (a.d == 128) return a.causal ? launch_fwd_bf16_pp<true, MODE>(a) : launch_fwd_bf16_pp<false, MODE>(a);
+  return a.causal ? launch_fwd_bf16_t<64, true, MODE>(a) : launch_fwd_bf16_t<64, false, MODE>(a);
 }
 
 hipError_t launch_fwd_bf16(const AttnArgs& a) {
-  const bool padded = a.kv_seqlens != nullptr;
-  if (a.d == 128) {
-    if (a.causal) return padded ? launch_fwd_bf16_pp<true, true>(a) : launch_fwd_bf16_pp<true, false>(a);
-    return padded ? launch_fwd_bf16_pp<false, true>(a) : launch_fwd_bf16_pp<false, false>(a);
-  }
-  if (a.causal) return padded ? launch_fwd_bf16_t<64, true, true>(a) : launch_fwd_bf16_t<64, true, false>(a);
-  return padded ? launch_fwd_bf16_t<64, false, true>(a) : launch_fwd_bf16_t<64, false, false>(a);
+  if (a.cu_q != nullptr) return launch_mode<kPacked>(a);
+  return a.kv_seqlens != nullptr ? launch_mode<kPadded>(a) : launch_mode<kDense>(a);
 }
 
 }  // namespace fa

@@ -21,6 +21,9 @@ struct F32Params {
   float* o_part;
   float* lse_part;
   const int32_t* kv_seqlens;
+  const int32_t* cu_q;  // packed variable-length layout when non-null
+  const int32_t* cu_k;
+  int total_q, total_k;
   int B, Hq, Hkv, Nq, Nk;
   int n_qtiles;
   int S;  // number of splits; 0 = final output
@@ -43,25 +46,39 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(F32Params p) {
   const int b = (int)(w / nsp);
   const int hk = hq / (p.Hq / p.Hkv);
 
-  const int kv_len = clamp_len(p.kv_seqlens, b, p.Nk);
+  // Rows of this sequence: dense / padded [B, H, N, d], or packed
+  // [H, total, d] with sequence b at rows cu[b] .. cu[b+1]-1.
+  int nq = p.Nq, nk = p.Nk, kv_len;
+  size_t q_row0, kv_base;
+  if (p.cu_q != nullptr) {
+    const int2 qr = packed_rows(p.cu_q, b, p.total_q), kr = packed_rows(p.cu_k, b, p.total_k);
+    nq = qr.y;
+    nk = kv_len = kr.y;
+    q_row0 = (size_t)hq * p.total_q + qr.x;
+    kv_base = (size_t)hk * p.total_k + kr.x;
+  } else {
+    kv_len = clamp_len(p.kv_seqlens, b, p.Nk);
+    q_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
+    kv_base = ((size_t)b * p.Hkv + hk) * (size_t)p.Nk;
+  }
   int ks = 0, ke = kv_len;
   if (p.S > 0) {
     const int chunk = split_chunk(kv_len, p.S, FA_DECODE_SPLIT_ALIGN);
     ks = min(split * chunk, kv_len);
     ke = min(ks + chunk, kv_len);
   }
-  const int diag = p.Nk - p.Nq;
+  const int diag = nk - nq;
   const int q0 = qt * BQ;
+  if (q0 >= nq) return;  // a packed sequence shorter than the longest one
   int kend = ke;
-  if (p.causal) kend = min(kend, min(q0 + BQ, p.Nq) - 1 + diag + 1);
+  if (p.causal) kend = min(kend, min(q0 + BQ, nq) - 1 + diag + 1);
 
   const int qrow = q0 + tid;
-  const size_t qo = ((size_t)b * p.Hq + hq) * (size_t)p.Nq + qrow;
-  const size_t kv_base = ((size_t)b * p.Hkv + hk) * (size_t)p.Nk;
+  const size_t qo = q_row0 + qrow;
   float q[D], o[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    q[d] = qrow < p.Nq ? p.q[qo * D + d] : 0.f;
+    q[d] = qrow < nq ? p.q[qo * D + d] : 0.f;
     o[d] = 0.f;
   }
   const int lim = p.causal ? min(ke, qrow + diag + 1) : ke;  // visible keys: [ks, lim)
@@ -107,7 +124,7 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(F32Params p) {
     m = m_new;
   }
 
-  if (qrow >= p.Nq) return;
+  if (qrow >= nq) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const float lse = l > 0.f ? m + logf(l) : kNegInf;
   if (p.S > 0) {
@@ -132,6 +149,10 @@ hipError_t launch_fwd_f32(const AttnArgs& a, const PartialOut* part) {
   p.o_part = part ? part->o_part : nullptr;
   p.lse_part = part ? part->lse_part : nullptr;
   p.kv_seqlens = a.kv_seqlens;
+  p.cu_q = a.cu_q;
+  p.cu_k = a.cu_k;
+  p.total_q = a.total_q;
+  p.total_k = a.total_k;
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
   p.n_qtiles = (a.Nq + 127) / 128;
   p.S = part ? part->num_splits : 0;

@@ -93,6 +93,34 @@ def make_inputs(config_id, *, B=None, Hq=None, Hkv=None, Nq=None, Nk=None, d=Non
     return q, k, v, lens
 
 
+TENSOR_PACKED = 100  # packed-layout tensors use tensor ids 100 + (q, k, v)
+
+
+def cumulative(lens):
+    """int32 offsets [0, l0, l0 + l1, ...] of packed sequences."""
+    out = torch.zeros(len(lens) + 1, dtype=torch.int32)
+    if len(lens):
+        out[1:] = torch.cumsum(torch.as_tensor(list(lens), dtype=torch.int64), 0).to(torch.int32)
+    return out
+
+
+def make_packed(config_id, lens_q, lens_k, Hq, Hkv, d, mult=1.0, dtype="bf16"):
+    """Packed variable-length inputs: q [Hq, total_q, d], k, v [Hkv, total_k, d]
+    (sequence b's rows drawn from their own seeded generator, then concatenated
+    along the token axis) and the int32 offsets cu_q, cu_k [B + 1]."""
+    tdt = _TORCH_DTYPE[dtype]
+
+    def cat(tensor_id, H, lens):
+        parts = [_slice(config_id, TENSOR_PACKED + tensor_id, b, (H, int(L), d), mult, tdt)
+                 for b, L in enumerate(lens)]
+        return torch.cat(parts, dim=1) if parts else torch.empty((H, 0, d), dtype=tdt)
+
+    q = cat(TENSOR_Q, Hq, lens_q)
+    k = cat(TENSOR_K, Hkv, lens_k)
+    v = cat(TENSOR_V, Hkv, lens_k)
+    return q, k, v, cumulative(lens_q), cumulative(lens_k)
+
+
 def make_dout(config_id, **overrides):
     """Seeded upstream gradient dL/dO shaped like a config's q (same value
     distribution as q), for the backward pass."""

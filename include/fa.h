@@ -85,6 +85,34 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            const int32_t* kv_seqlens, int dtype, void* stream);
 
 /*
+ * fa_fwd_varlen -- fa_fwd over packed variable-length sequences (varlen and
+ * chunked prefill).  The pages put padding masks inside the tile and set
+ * prompt processing apart from one-token decode against a KV cache (concept
+ * note, section "是什么" and its list of misconceptions); they fix no packed
+ * layout.  Here the B sequences of a batch are concatenated along the token
+ * axis of every head:
+ *   q [Hq, total_q, d] in     k, v [Hkv, total_k, d] in     o [Hq, total_q, d] out
+ *   lse [Hq, total_q] float32 out
+ *   cu_seqlens_q, cu_seqlens_k: DEVICE int32[B + 1], non-decreasing, from 0
+ *   to total_q (total_k): sequence b owns query rows cu_seqlens_q[b] ..
+ *   cu_seqlens_q[b+1] - 1 and key rows cu_seqlens_k[b] .. cu_seqlens_k[b+1] - 1,
+ *   and attends only to its own keys.
+ *   max_seqlen_q: at least the longest query sequence (it sizes the grid).
+ * Each sequence is fa_fwd with Nq = Lq_b, Nk = Lk_b, so under causal = 1 the
+ * mask is bottom-right aligned per sequence: local key j is visible to local
+ * query i iff j <= i + Lk_b - Lq_b -- a chunk of Lq_b new queries sees the
+ * Lk_b - Lq_b cached keys before it.  Offsets cannot be checked without a
+ * sync: the kernels clamp them to [0, total] and read a decreasing pair as an
+ * empty sequence, so no row outside the tensors is addressed; query rows of a
+ * sequence longer than max_seqlen_q, and rows outside every sequence, are not
+ * written.  dtype, d, scale, GQA and alignment as for fa_fwd.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int Hq, int Hkv,
+                  int total_q, int total_k, int max_seqlen_q, int d, float scale, int causal, int dtype,
+                  void* stream);
+
+/*
  * fa_decode_workspace_bytes -- bytes of device workspace fa_decode needs:
  * float32 partial outputs [B,Hq,num_splits,d] followed (at a 256-byte aligned
  * offset) by float32 partial LSEs [B,Hq,num_splits].  Returns 0 for invalid

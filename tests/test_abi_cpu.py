@@ -169,3 +169,26 @@ def paged(lib, q=P, kp=P, vp=P, table=P, o=P, lse=P, B=2, Hq=8, Hkv=2, num_pages
 ])
 def test_paged_rejects(lib, kwargs, status):
     assert paged(lib, **kwargs) == status
+
+
+def varlen(lib, q=P, k=P, v=P, o=P, lse=P, cu_q=P, cu_k=P, B=2, Hq=4, Hkv=2, total_q=40, total_k=50, max_q=30,
+           d=128, scale=0.125, causal=1, dtype=1):
+    return lib.fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, B, Hq, Hkv, total_q, total_k, max_q, d, scale, causal,
+                             dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(cu_q=None), BAD), (dict(cu_k=None), BAD), (dict(cu_q=P + 2), BAD), (dict(max_q=-1), BAD),
+    (dict(total_q=-1), BAD), (dict(total_k=-1), BAD), (dict(B=-1), BAD), (dict(q=None), BAD),
+    (dict(o=P + 8), BAD), (dict(lse=None), BAD), (dict(k=None), BAD), (dict(v=P + 4), BAD),
+    (dict(causal=2), BAD), (dict(scale=0.0), BAD), (dict(d=96), UNSUP), (dict(dtype=5), UNSUP),
+    (dict(Hq=3), UNSUP)])
+def test_varlen_rejects(lib, kwargs, status):
+    assert varlen(lib, **kwargs) == status, lib.fa_last_error()
+    assert lib.fa_last_error() != b""
+
+
+@pytest.mark.parametrize("kwargs", [dict(total_q=0, q=None, o=None, lse=None), dict(max_q=0), dict(B=0),
+                                    dict(Hq=0, Hkv=0)])
+def test_varlen_empty_is_noop(lib, kwargs):
+    assert varlen(lib, **kwargs) == 0, lib.fa_last_error()
