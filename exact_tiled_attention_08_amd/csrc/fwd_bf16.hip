@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   const SeqRows sr = seq_rows<MODE>(p, b, hq, hk);
   const int nq = sr.nq, kv_len = sr.kv_len;
   const int q0 = qt * BM;
-  if (q0 >= nq) return;  // a packed sequence shorter than the longest one
+  if (MODE == kPacked && q0 >= nq) return;  // a sequence shorter than the longest one
   const int diag = sr.nk - nq;  // key j visible to row i iff j <= i + diag
   int kend = kv_len;
   if (CAUSAL) {
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const SeqRows sr = seq_rows<MODE>(p, b, hq, hk);
   const int nq = sr.nq, kv_len = sr.kv_len;
   const int q0 = qt * BM;
-  if (q0 >= nq) return;  // a packed sequence shorter than the longest one
+  if (MODE == kPacked && q0 >= nq) return;  // a sequence shorter than the longest one
   const int diag = sr.nk - nq;
   int kend = kv_len;
   if (CAUSAL) kend = min(kend, min(q0 + BM, nq) - 1 + diag + 1);
