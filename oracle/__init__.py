@@ -23,3 +23,4 @@ from .attention import (  # noqa: F401
     paged_to_contiguous,
     to_f64,
 )
+from .fp8 import decode_fp8, attention_fp8_ref, E4M3, E5M2  # noqa: F401

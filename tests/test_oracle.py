@@ -375,12 +375,51 @@ def check_varlen_equal_lengths():
         assert np.allclose(LSE, np.concatenate(list(L_b), axis=1), atol=1e-12, rtol=0)
 
 
+_TORCH_FP8 = {oracle.E4M3: torch.float8_e4m3fn, oracle.E5M2: torch.float8_e5m2}
+
+
+def check_fp8_decode_against_torch():
+    # every code of both formats against torch's own float8 types
+    codes = np.arange(256)
+    for fmt, tdt in _TORCH_FP8.items():
+        ref = torch.arange(256, dtype=torch.uint8).view(tdt).to(torch.float64).numpy()
+        assert np.array_equal(oracle.decode_fp8(codes, fmt), ref, equal_nan=True), fmt
+
+
+def check_fp8_decode_closed_forms():
+    # values fixed by the format definitions: ones, largest finite, smallest
+    # normal and subnormal, infinities and NaNs
+    e4 = {0x38: 1.0, 0xB8: -1.0, 0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9,
+          0x00: 0.0, 0x40: 2.0, 0x3C: 1.5}
+    e5 = {0x3C: 1.0, 0x7B: 57344.0, 0x04: 2.0 ** -14, 0x01: 2.0 ** -16, 0x7C: np.inf, 0xFC: -np.inf,
+          0x3E: 1.5, 0x80: -0.0}
+    for fmt, table in ((oracle.E4M3, e4), (oracle.E5M2, e5)):
+        got = oracle.decode_fp8(np.array(list(table)), fmt)
+        assert np.array_equal(got, np.array(list(table.values()))), (fmt, got)
+    assert np.isnan(oracle.decode_fp8(np.array([0x7F, 0xFF]), oracle.E4M3)).all()
+    assert np.isnan(oracle.decode_fp8(np.array([0x7D, 0x7E, 0x7F, 0xFF]), oracle.E5M2)).all()
+
+
+def check_fp8_attention_dequantised():
+    # attention on FP8 codes equals attention on the inputs dequantised by torch
+    g = torch.Generator().manual_seed(3)
+    for fmt, tdt in _TORCH_FP8.items():
+        x = [torch.randn(shape, generator=g) * 3 for shape in ((1, 4, 9, 8), (1, 2, 11, 8), (1, 2, 11, 8))]
+        codes = [t.to(tdt).view(torch.uint8) for t in x]
+        ds = (0.5, 0.25, 2.0)
+        O, L = oracle.attention_fp8_ref(*codes, fmt, *ds, causal=True, scale=0.3)
+        deq = [c.view(tdt).to(torch.float64).numpy() * s for c, s in zip(codes, ds)]
+        O2, L2 = oracle.attention_ref(*deq, causal=True, scale=0.3)
+        assert np.allclose(O, O2, atol=1e-12, rtol=0) and np.allclose(L, L2, atol=1e-12, rtol=0), fmt
+
+
 PIN_CHECKS = [check_rows_sum_to_one, check_constant_v, check_single_key, check_causal_row0,
               check_zero_q_closed_form, check_two_keys, check_blocked_recurrence,
               check_key_permutation, check_gqa_equals_mha, check_against_torch_sdpa,
               check_merge_identity, check_split_bounds, check_bwd_finite_differences,
               check_bwd_against_autograd, check_bwd_invariants, check_paged_gather,
-              check_varlen_brute_force, check_varlen_chunked_prefill, check_varlen_equal_lengths]
+              check_varlen_brute_force, check_varlen_chunked_prefill, check_varlen_equal_lengths,
+              check_fp8_decode_against_torch, check_fp8_decode_closed_forms, check_fp8_attention_dequantised]
 
 
 @pytest.mark.parametrize("check", PIN_CHECKS, ids=lambda f: f.__name__)
@@ -531,9 +570,39 @@ def _mut_varlen_keys_at_q_offsets(q, k, v, cu_q, cu_k, causal=False, scale=None)
     return _varlen_variant(q, k, v, cu_q, cu_k, causal, scale, keys_at_q_offsets=True)
 
 
+def _fp8_variant(codes, fmt, bias_shift=0, sub_exp_shift=0):
+    from oracle import fp8 as F
+    ebits, mbits, bias = F._FIELDS[fmt]
+    bias += bias_shift
+    c = np.asarray(A.to_f64(codes), dtype=np.int64) & 0xFF
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> mbits) & ((1 << ebits) - 1)
+    frac = (c & ((1 << mbits) - 1)) / (1 << mbits)
+    out = np.where(e == 0, sign * frac * np.exp2(1.0 - bias + sub_exp_shift), sign * (1 + frac) * np.exp2(e - bias))
+    emax = (1 << ebits) - 1
+    if fmt == F.E4M3:
+        return np.where((e == emax) & (frac == 1 - 1 / (1 << mbits)), np.nan, out)
+    return np.where(e == emax, np.where(frac == 0, sign * np.inf, np.nan), out)
+
+
+def _mut_fp8_bias(codes, fmt):
+    return _fp8_variant(codes, fmt, bias_shift=1)
+
+
+def _mut_fp8_subnormal_exponent(codes, fmt):
+    return _fp8_variant(codes, fmt, sub_exp_shift=-1)
+
+
+def _mut_fp8_v_not_descaled(q, k, v, fmt, q_descale, k_descale, v_descale, causal=False, kv_seqlens=None,
+                            scale=None):
+    return _ORIG_FP8_ATT(q, k, v, fmt, q_descale, k_descale, 1.0, causal=causal, kv_seqlens=kv_seqlens,
+                         scale=scale)
+
+
 _ORIG_PAGED = A.paged_to_contiguous
 _ORIG_ONE_HEAD = A._one_head
 _ORIG_MERGE = A.merge_partials
+_ORIG_FP8_ATT = oracle.attention_fp8_ref
 
 MUTANTS = [("_allowed", _mut_causal_off_by_one), ("_allowed", _mut_padding_inclusive),
            ("_head_map", _mut_head_modulo), ("_one_head", _mut_lse_drops_max),
@@ -542,13 +611,20 @@ MUTANTS = [("_allowed", _mut_causal_off_by_one), ("_allowed", _mut_padding_inclu
            ("attention_bwd_ref", _mut_bwd_unscaled_dq), ("attention_bwd_ref", _mut_bwd_gqa_overwrite),
            ("paged_to_contiguous", _mut_paged_row_reversed),
            ("attention_varlen_ref", _mut_varlen_top_left),
-           ("attention_varlen_ref", _mut_varlen_keys_at_q_offsets)]
+           ("attention_varlen_ref", _mut_varlen_keys_at_q_offsets),
+           ("decode_fp8", _mut_fp8_bias), ("decode_fp8", _mut_fp8_subnormal_exponent),
+           ("attention_fp8_ref", _mut_fp8_v_not_descaled)]
 
 
 @pytest.mark.parametrize("name,mutant", MUTANTS, ids=lambda x: getattr(x, "__name__", x))
 def test_pins_catch_planted_mistake(monkeypatch, name, mutant):
-    monkeypatch.setattr(A, name, mutant)
-    if name in ("merge_partials", "attention_bwd_ref", "paged_to_contiguous", "attention_varlen_ref"):
+    from oracle import fp8 as F
+    if name in ("decode_fp8", "attention_fp8_ref"):
+        monkeypatch.setattr(F, name, mutant)
+    else:
+        monkeypatch.setattr(A, name, mutant)
+    if name in ("merge_partials", "attention_bwd_ref", "paged_to_contiguous", "attention_varlen_ref",
+                "decode_fp8", "attention_fp8_ref"):
         monkeypatch.setattr(oracle, name, mutant)
     failed = []
     for check in PIN_CHECKS:
