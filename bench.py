@@ -23,6 +23,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (N=8K causal d=128); decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU (published 2.5 PFLOP/s)
+PEAK_FP8_TFLOPS = 5033.2   # dense FP8 MFMA: twice the bf16 rate (published 5.0 PFLOP/s)
+# The FP8 forward runs Q.K^T on FP8 and P.V on bf16 matrix cores, half of its
+# FLOP each: at both peaks one FLOP costs (1/2)/PEAK_FP8 + (1/2)/PEAK_BF16.
+PEAK_FP8_BF16_MIX_TFLOPS = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
 PEAK_HBM_GBS = 8000.0      # HBM3E, 8 TB/s
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
 KERNEL_SOURCES = ["fwd_bf16.hip", "decode_bf16.hip", "fa_device.hpp"]
@@ -128,6 +132,8 @@ def main():
                     help="timed paged-cache decode calls (0 = skip the paged decode)")
     ap.add_argument("--varlen-steps", type=int, default=20,
                     help="timed packed variable-length and chunked prefill calls (0 = skip them)")
+    ap.add_argument("--fp8-steps", type=int, default=20,
+                    help="timed FP8 (E4M3) prefill calls on the long-context shape (0 = skip)")
     ap.add_argument("--only", choices=["prefill", "decode", "backward", "copy"], default=None,
                     help="profiling aid: run only one part of the step (or a 1 GiB device copy used to "
                          "calibrate the HBM byte counters) and print no JSON")
@@ -302,6 +308,34 @@ def main():
             print(f"[bench] varlen {name}: {v_ms:.3f} ms, {v_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
             del qv, kv_, vv, ov, lv
 
+    fp8 = None
+    if args.fp8_steps > 0:
+        # The long-context prefill on E4M3 inputs (per-tensor quantised).
+        q8, k8, v8, _, ds8 = inputs.make_fp8_inputs(3, "e4m3")
+        q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
+        for _ in range(10):
+            fa.fa_fwd_fp8(q8, k8, v8, *ds8, causal=True, out=o3, lse=l3)
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.fp8_steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in fev:
+            e0.record(stream)
+            fa.fa_fwd_fp8(q8, k8, v8, *ds8, causal=True, out=o3, lse=l3)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        f8_ms = sum(e0.elapsed_time(e1) for e0, e1 in fev) / len(fev)
+        f8_flop = prefill_flops(c3["B"], c3["Hq"], c3["Nq"], c3["Nk"], c3["d"], True)
+        f8_tf = f8_flop / (f8_ms * 1e-3) / 1e12
+        fp8 = {"value": round(f8_tf, 2), "unit": "TFLOP/s", "avg_call_ms": round(f8_ms, 5), "flop_per_call": f8_flop,
+               "workload": "fa_fwd_fp8 E4M3 B=1 H=32 N=8192 d=128 causal (per-tensor descales), bf16 output",
+               "roofline": {"bound": "mfma", "kernel": "fwd_fp8_pp_kernel<e4m3,causal>", "achieved": round(f8_tf, 2),
+                            "peak": round(PEAK_FP8_BF16_MIX_TFLOPS, 1), "unit": "TFLOP/s",
+                            "peak_note": "Q.K^T at the FP8 peak (5033 TFLOP/s), P.V at the bf16 peak (2517)",
+                            "frac": round(f8_tf / PEAK_FP8_BF16_MIX_TFLOPS, 4),
+                            "frac_of_fp8_peak": round(f8_tf / PEAK_FP8_TFLOPS, 4), "traffic": None}}
+        print(f"[bench] fp8 prefill: {f8_ms:.3f} ms, {f8_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        del q8, k8, v8
+
     fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
     split_ms = [e[1].elapsed_time(e[2]) for e in events]
     merge_ms = [e[2].elapsed_time(e[3]) for e in events]
@@ -359,6 +393,7 @@ def main():
         "backward": bwd,
         "decode_paged": paged,
         "prefill_varlen": varlen,
+        "prefill_fp8": fp8,
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -13,7 +13,7 @@ import torch
 from . import _lib
 from ._lib import FAError, FA_DECODE_SPLIT_ALIGN, FA_MAX_SPLITS  # noqa: F401
 
-__all__ = ["fa_fwd", "fa_fwd_varlen", "fa_decode_splitkv", "fa_lse_merge", "fa_decode", "fa_decode_workspace_bytes",
+__all__ = ["fa_fwd", "fa_fwd_fp8", "fa_fwd_varlen", "fa_decode_splitkv", "fa_lse_merge", "fa_decode", "fa_decode_workspace_bytes",
            "fa_decode_paged", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_last_error", "FAError",
            "default_scale"]
 
@@ -83,6 +83,43 @@ def fa_fwd(q, k, v, causal=False, kv_seqlens=None, scale=None, out=None, lse=Non
     lib = _lib.load()
     _lib.check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, s,
                           int(bool(causal)), _ptr(lens), _DTYPES[q.dtype], _stream(q)))
+    return out, lse
+
+
+_FP8 = {torch.float8_e4m3fn: _lib.FA_FP8_E4M3, torch.float8_e5m2: _lib.FA_FP8_E5M2}
+
+
+def fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False, kv_seqlens=None, scale=None, out=None,
+               lse=None):
+    """Exact attention on FP8 inputs (d = 128).
+
+    q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] are torch float8_e4m3fn or float8_e5m2
+    tensors (one format for all three); the real inputs are descale * value.
+    Returns (o [B,Hq,Nq,d] bfloat16, lse [B,Hq,Nq] float32).
+    """
+    _check_tensor(q, "q", ndim=4)
+    if q.dtype not in _FP8:
+        raise ValueError("q must be float8_e4m3fn or float8_e5m2")
+    _check_tensor(k, "k", q.dtype, 4, q.device)
+    _check_tensor(v, "v", q.dtype, 4, q.device)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, Hkv, Nk, d] matching q")
+    lens = _lens(kv_seqlens, B, q.device)
+    if out is None:
+        out = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check_tensor(out, "out", torch.bfloat16, 4, q.device)
+    _check_tensor(lse, "lse", torch.float32, 3, q.device)
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("out/lse have the wrong shape")
+    s = default_scale(d) if scale is None else float(scale)
+    lib = _lib.load()
+    _lib.check(lib.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, s,
+                              int(bool(causal)), _ptr(lens), float(q_descale), float(k_descale), float(v_descale),
+                              _FP8[q.dtype], _stream(q)))
     return out, lse
 
 

@@ -9,7 +9,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
-FA_F32, FA_BF16 = 0, 1
+FA_F32, FA_BF16, FA_FP8_E4M3, FA_FP8_E5M2 = 0, 1, 2, 3
 FA_DECODE_SPLIT_ALIGN = 128
 FA_MAX_SPLITS = 256
 
@@ -18,6 +18,7 @@ _p, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 # name -> (restype, argtypes); mirrors include/fa.h
 PROTOTYPES = {
     "fa_fwd": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _i, _p]),
+    "fa_fwd_fp8": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _f, _f, _f, _i, _p]),
     "fa_fwd_varlen": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _p]),
     "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "fa_decode_splitkv": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _i, _i, _p]),

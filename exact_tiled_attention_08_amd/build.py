@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fwd_bf16.hip", "decode_bf16.hip", "fwd_f32.hip", "bwd_bf16.hip", "api.cpp"]
+SOURCES = ["fwd_bf16.hip", "fwd_fp8.hip", "decode_bf16.hip", "fwd_f32.hip", "bwd_bf16.hip", "api.cpp"]
 ARCH = "gfx950"
 
 # Packed-FP32 instruction forms are kept out of every kernel.  LDS addresses

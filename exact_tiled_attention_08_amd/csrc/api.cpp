@@ -131,6 +131,34 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return hip_status(fa::launch_fwd_f32(a, nullptr), "fa_fwd (f32) launch");
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
+               int Nk, int d, float scale, int causal, const int32_t* kv_seqlens, float q_descale, float k_descale,
+               float v_descale, int dtype, void* stream) {
+  if (dtype != FA_FP8_E4M3 && dtype != FA_FP8_E5M2)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_fp8 takes dtype FA_FP8_E4M3 or FA_FP8_E5M2, got %d", dtype);
+  int st = check_common(B, Hq, Hkv, Nq, Nk, d, scale, FA_BF16);
+  if (st != FA_OK) return st;
+  if (d != 128) return fail(FA_ERR_UNSUPPORTED, "fa_fwd_fp8 supports head dim 128 only (got %d)", d);
+  for (float ds : {q_descale, k_descale, v_descale})
+    if (!(std::isfinite(ds) && ds > 0.f)) return fail(FA_ERR_INVALID_ARG, "descales must be finite and > 0");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if ((long long)B * Hq * Nq == 0) return ok();
+  if ((st = check_ptr(q, 16, "q")) != FA_OK) return st;
+  if ((st = check_ptr(o, 16, "o")) != FA_OK) return st;
+  if ((st = check_ptr(lse, 4, "lse")) != FA_OK) return st;
+  if (Nk > 0) {
+    if ((st = check_ptr(k, 16, "k")) != FA_OK) return st;
+    if ((st = check_ptr(v, 16, "v")) != FA_OK) return st;
+  }
+  if (kv_seqlens != nullptr && !aligned(kv_seqlens, 4))
+    return fail(FA_ERR_INVALID_ARG, "kv_seqlens is not 4-byte aligned");
+  const long long tiles = ((long long)Nq + 255) / 256 * B * Hq;
+  if (tiles > 0x7fffffffLL) return fail(FA_ERR_UNSUPPORTED, "problem too large for one launch");
+  fa::AttnArgs a = make_args(q, k, v, o, lse, kv_seqlens, B, Hq, Hkv, Nq, Nk, d, scale, causal, stream);
+  return hip_status(fa::launch_fwd_fp8(a, dtype == FA_FP8_E5M2, fa::Fp8Scales{q_descale, k_descale, v_descale}),
+                    "fa_fwd_fp8 launch");
+}
+
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens_q,
                   const int32_t* cu_seqlens_k, int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
                   int d, float scale, int causal, int dtype, void* stream) {

@@ -52,6 +52,13 @@ hipError_t launch_decode_splitkv_bf16(const AttnArgs& a, const PartialOut& part,
 hipError_t launch_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
                             int rows, int d, int num_splits, bool out_bf16, hipStream_t stream);
 
+// FP8 prefill forward (d = 128): q, k, v hold FP8 codes (E4M3, or E5M2 when
+// e5m2 != 0) whose real values are descale * value(code); o is bf16.
+struct Fp8Scales {
+  float q_descale, k_descale, v_descale;
+};
+hipError_t launch_fwd_fp8(const AttnArgs& a, int e5m2, const Fp8Scales& sc);
+
 // Backward pass (bf16): gradients of fa_fwd's output.
 struct BwdArgs {
   const void* q;

@@ -121,6 +121,30 @@ def make_packed(config_id, lens_q, lens_k, Hq, Hkv, d, mult=1.0, dtype="bf16"):
     return q, k, v, cumulative(lens_q), cumulative(lens_k)
 
 
+FP8_DTYPES = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+
+
+def quantize_fp8(x, fmt):
+    """Per-tensor FP8 quantisation of a float tensor: descale = amax / (largest
+    finite code), codes = x / descale rounded to nearest-even in the format.
+    Returns (codes as a torch float8 tensor, descale as a Python float holding
+    a float32 value); the real input the codes stand for is descale * codes."""
+    x = x.to(torch.float32)
+    amax = float(x.abs().max()) if x.numel() else 0.0
+    descale = float(torch.tensor(amax / FP8_MAX[fmt] if amax > 0 else 1.0, dtype=torch.float32))
+    return (x / descale).to(FP8_DTYPES[fmt]), descale
+
+
+def make_fp8_inputs(config_id, fmt, **overrides):
+    """FP8 versions of a config's q, k, v: the config's float32 draws (before
+    any bf16 rounding), each quantised per tensor.  Returns
+    (q, k, v, kv_seqlens, (q_descale, k_descale, v_descale))."""
+    q, k, v, lens = make_inputs(config_id, dtype="f32", **overrides)
+    (qc, qs), (kc, ks), (vc, vs) = (quantize_fp8(t, fmt) for t in (q, k, v))
+    return qc, kc, vc, lens, (qs, ks, vs)
+
+
 def make_dout(config_id, **overrides):
     """Seeded upstream gradient dL/dO shaped like a config's q (same value
     distribution as q), for the backward pass."""

@@ -59,7 +59,7 @@ enum fa_status {
   FA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
 };
 
-enum fa_dtype { FA_F32 = 0, FA_BF16 = 1 };
+enum fa_dtype { FA_F32 = 0, FA_BF16 = 1, FA_FP8_E4M3 = 2, FA_FP8_E5M2 = 3 };
 
 /* Split-KV decode partitions each sequence's keys [0, L) into num_splits
  * chunks of C = ceil(L / num_splits) keys, C rounded up to a multiple of
@@ -83,6 +83,31 @@ enum fa_dtype { FA_F32 = 0, FA_BF16 = 1 };
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
            const int32_t* kv_seqlens, int dtype, void* stream);
+
+/*
+ * fa_fwd_fp8 -- fa_fwd on FP8 inputs.  The pages credit FP8 matrix units for
+ * part of FlashAttention-3's throughput (2026 explainer, section "二代和三代")
+ * without fixing formats or scaling; here q, k and v hold 8-bit OCP
+ * floating-point codes of one format (dtype FA_FP8_E4M3 or FA_FP8_E5M2), and
+ * each tensor has one float32 descale, so the real inputs are
+ * q_descale * value(q code), and likewise for k and v.  The attention of those
+ * real inputs is computed as by fa_fwd: S = Q K^T on the FP8 matrix cores
+ * (float32 accumulators, both descales folded into the softmax scale; the
+ * instruction's internal sums are less precise than float32 -- measured
+ * errors up to ~2^-15 of sum_d |q_d k_d|); V converted exactly to bf16 and
+ * O = P V on the bf16 matrix cores with P rounded to bf16; O multiplied by
+ * v_descale at the end.
+ *   q [B,Hq,Nq,d], k, v [B,Hkv,Nk,d]: FP8 codes (one byte each), in
+ *   o [B,Hq,Nq,d] bf16 out, lse [B,Hq,Nq] float32 out
+ *   q_descale, k_descale, v_descale: finite and > 0.
+ * d must be 128.  scale, causal, kv_seqlens, GQA, alignment (16 bytes for
+ * q, k, v, o) and errors as for fa_fwd.  NaN or infinite codes propagate as
+ * IEEE arithmetic does.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+               const int32_t* kv_seqlens, float q_descale, float k_descale, float v_descale,
+               int dtype, void* stream);
 
 /*
  * fa_fwd_varlen -- fa_fwd over packed variable-length sequences (varlen and

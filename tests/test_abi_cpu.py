@@ -41,7 +41,8 @@ def test_header_constants_match_binding():
     assert int(re.search(r"#define FA_DECODE_SPLIT_ALIGN (\d+)", text).group(1)) == _lib.FA_DECODE_SPLIT_ALIGN
     assert int(re.search(r"#define FA_MAX_SPLITS (\d+)", text).group(1)) == _lib.FA_MAX_SPLITS
     for name, val in [("FA_OK", 0), ("FA_ERR_INVALID_ARG", -1), ("FA_ERR_UNSUPPORTED", -2),
-                      ("FA_ERR_WORKSPACE", -3), ("FA_ERR_HIP", -4), ("FA_F32", 0), ("FA_BF16", 1)]:
+                      ("FA_ERR_WORKSPACE", -3), ("FA_ERR_HIP", -4), ("FA_F32", 0), ("FA_BF16", 1),
+                      ("FA_FP8_E4M3", 2), ("FA_FP8_E5M2", 3)]:
         assert re.search(rf"\b{name} = {val}\b", text), name
 
 
@@ -192,3 +193,24 @@ def test_varlen_rejects(lib, kwargs, status):
                                     dict(Hq=0, Hkv=0)])
 def test_varlen_empty_is_noop(lib, kwargs):
     assert varlen(lib, **kwargs) == 0, lib.fa_last_error()
+
+
+def fwd_fp8(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Nq=16, Nk=16, d=128, scale=0.125, causal=0,
+            lens=None, qd=0.5, kd=0.5, vd=0.5, dtype=2):
+    return lib.fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, lens, qd, kd, vd, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=1), UNSUP), (dict(dtype=0), UNSUP), (dict(dtype=4), UNSUP), (dict(d=64), UNSUP),
+    (dict(Hq=3), UNSUP), (dict(qd=0.0), BAD), (dict(kd=-1.0), BAD), (dict(vd=float("nan")), BAD),
+    (dict(vd=float("inf")), BAD), (dict(scale=0.0), BAD), (dict(causal=2), BAD), (dict(q=None), BAD),
+    (dict(k=P + 8), BAD), (dict(o=None), BAD), (dict(lse=P + 2), BAD), (dict(lens=P + 1), BAD),
+    (dict(B=-1), BAD)])
+def test_fp8_rejects(lib, kwargs, status):
+    assert fwd_fp8(lib, **kwargs) == status, lib.fa_last_error()
+    assert lib.fa_last_error() != b""
+
+
+@pytest.mark.parametrize("kwargs", [dict(B=0), dict(Nq=0, q=None, o=None, lse=None), dict(dtype=3, Hq=0)])
+def test_fp8_empty_is_noop(lib, kwargs):
+    assert fwd_fp8(lib, **kwargs) == _lib.FA_OK, lib.fa_last_error()
