@@ -29,7 +29,7 @@ PEAK_FP8_TFLOPS = 5033.2   # dense FP8 MFMA: twice the bf16 rate (published 5.0 
 PEAK_FP8_BF16_MIX_TFLOPS = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
 PEAK_HBM_GBS = 8000.0      # HBM3E, 8 TB/s
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
-KERNEL_SOURCES = ["fwd_bf16.hip", "decode_bf16.hip", "fa_device.hpp"]
+KERNEL_SOURCES = ["fwd_bf16.hip", "fwd_fp8.hip", "decode_bf16.hip", "bwd_bf16.hip", "fa_device.hpp"]
 
 
 def kernel_source_hash():
@@ -105,6 +105,24 @@ def profile_only(args, dev):
         q, k, v = [t.to(dev) for t in inputs.make_inputs(3)[:3]]
         for _ in range(args.warmup + args.steps):
             fa.fa_fwd(q, k, v, causal=True)
+    elif args.only == "fp8":
+        q, k, v, _, ds = inputs.make_fp8_inputs(3, "e4m3")
+        q, k, v = q.to(dev), k.to(dev), v.to(dev)
+        for _ in range(args.warmup + args.steps):
+            fa.fa_fwd_fp8(q, k, v, *ds, causal=True)
+    elif args.only == "varlen":
+        lens = inputs.lengths(4, 4, 2048, 4096).tolist()
+        q, k, v, cq, ck = (t.to(dev) for t in inputs.make_packed(4, lens, lens, 32, 8, 128))
+        for _ in range(args.warmup + args.steps):
+            fa.fa_fwd_varlen(q, k, v, cq, ck, max(lens), causal=True)
+    elif args.only == "paged":
+        c5 = inputs.CONFIGS[5]
+        q, k, v = [t.to(dev) for t in inputs.make_inputs(5)[:3]]
+        kp, vp, table = paged_copy(k, v, 16, dev)
+        lens = torch.full((c5["B"],), c5["Nk"], dtype=torch.int32, device=dev)
+        del k, v
+        for _ in range(args.warmup + args.steps):
+            fa.fa_decode_paged(q, kp, vp, table, lens, num_splits=c5["num_splits"])
     elif args.only == "backward":
         q, k, v = [t.to(dev) for t in inputs.make_inputs(3)[:3]]
         do = inputs.make_dout(3).to(dev)
@@ -118,6 +136,36 @@ def profile_only(args, dev):
             fa.fa_decode(q, k, v, num_splits=c5["num_splits"])
     torch.cuda.synchronize()
     print(f"[bench] ran {args.only} x{args.warmup + args.steps}", file=sys.stderr, flush=True)
+
+
+def warm(call, seconds=0.25):
+    """Run `call` back to back for about `seconds` (clocks settle after a
+    change of workload), synchronising every 10 calls."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            call()
+        n += 10
+        torch.cuda.synchronize()
+    return n
+
+
+def paged_copy(k, v, page, dev):
+    """The cache [B, Hkv, Nk, d] scattered into a shuffled pool of pages
+    [B*Nk/page, Hkv, page, d] and its block table."""
+    import torch
+    B, Hkv, Nk, d = k.shape
+    n_pages = B * (Nk // page)
+    g = torch.Generator(device=dev).manual_seed(555)
+    table = torch.randperm(n_pages, generator=g, device=dev).to(torch.int32).reshape(B, Nk // page)
+    idx = table.long().reshape(-1)
+    kp = torch.empty((n_pages, Hkv, page, d), dtype=k.dtype, device=dev)
+    vp = torch.empty_like(kp)
+    kp[idx] = k.reshape(B, Hkv, Nk // page, page, d).permute(0, 2, 1, 3, 4).reshape(-1, Hkv, page, d)
+    vp[idx] = v.reshape(B, Hkv, Nk // page, page, d).permute(0, 2, 1, 3, 4).reshape(-1, Hkv, page, d)
+    return kp, vp, table
 
 
 def main():
@@ -134,7 +182,8 @@ def main():
                     help="timed packed variable-length and chunked prefill calls (0 = skip them)")
     ap.add_argument("--fp8-steps", type=int, default=20,
                     help="timed FP8 (E4M3) prefill calls on the long-context shape (0 = skip)")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "fp8", "varlen", "paged", "copy"],
+                    default=None,
                     help="profiling aid: run only one part of the step (or a 1 GiB device copy used to "
                          "calibrate the HBM byte counters) and print no JSON")
     args = ap.parse_args()
@@ -212,9 +261,8 @@ def main():
         ws = torch.empty(fa.fa_bwd_workspace_bytes(c3["B"], c3["Hq"], c3["Nq"], c3["d"]), dtype=torch.uint8,
                          device=dev)
         dq3, dk3, dv3 = torch.empty_like(q3), torch.empty_like(k3), torch.empty_like(v3)
-        print(f"[bench] backward: warmup 10, timing {args.bwd_steps}", file=sys.stderr, flush=True)
-        for _ in range(10):
-            fa.fa_bwd(q3, k3, v3, o3, l3, do3, causal=True, workspace=ws, dq=dq3, dk=dk3, dv=dv3)
+        print(f"[bench] backward: warmup 0.25 s, timing {args.bwd_steps}", file=sys.stderr, flush=True)
+        warm(lambda: fa.fa_bwd(q3, k3, v3, o3, l3, do3, causal=True, workspace=ws, dq=dq3, dk=dk3, dv=dv3))
         bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.bwd_steps)]
         torch.cuda.synchronize()
@@ -233,26 +281,19 @@ def main():
                "avg_call_ms": round(bwd_ms, 5),
                "roofline": {"bound": "mfma", "kernel": "bwd_rowdot + bwd_dq_kernel + bwd_dkdv_kernel",
                             "achieved": round(bwd_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                            "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+                            "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+                            "traffic": load_traffic("bwd_rowdot+bwd_dq+bwd_dkdv")}}
 
     paged = None
     if args.paged_steps > 0:
         # The same decode over a paged copy of the cache: 16-key pages in a
         # shuffled pool, read through a block table.
         page = 16
-        n_pages = B5 * (Nk5 // page)
-        g = torch.Generator(device=dev).manual_seed(555)
-        table = torch.randperm(n_pages, generator=g, device=dev).to(torch.int32).reshape(B5, Nk5 // page)
-        kp = torch.empty((n_pages, Hkv5, page, d5), dtype=torch.bfloat16, device=dev)
-        vp = torch.empty_like(kp)
-        idx = table.long().reshape(-1)
-        kp[idx] = k5.reshape(B5, Hkv5, Nk5 // page, page, d5).permute(0, 2, 1, 3, 4).reshape(-1, Hkv5, page, d5)
-        vp[idx] = v5.reshape(B5, Hkv5, Nk5 // page, page, d5).permute(0, 2, 1, 3, 4).reshape(-1, Hkv5, page, d5)
+        kp, vp, table = paged_copy(k5, v5, page, dev)
         lens5 = torch.full((B5,), Nk5, dtype=torch.int32, device=dev)
         wsp = torch.empty(fa.fa_decode_workspace_bytes(B5, Hq5, d5, S), dtype=torch.uint8, device=dev)
-        print(f"[bench] paged decode: warmup 10, timing {args.paged_steps}", file=sys.stderr, flush=True)
-        for _ in range(10):
-            fa.fa_decode_paged(q5, kp, vp, table, lens5, num_splits=S, workspace=wsp, out=o5, lse=l5)
+        print(f"[bench] paged decode: warmup 0.25 s, timing {args.paged_steps}", file=sys.stderr, flush=True)
+        warm(lambda: fa.fa_decode_paged(q5, kp, vp, table, lens5, num_splits=S, workspace=wsp, out=o5, lse=l5))
         pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.paged_steps)]
         torch.cuda.synchronize()
@@ -269,7 +310,8 @@ def main():
                              "shuffled pool",
                  "algorithmic_bytes": pbytes, "avg_call_ms": round(p_ms, 5),
                  "roofline": {"bound": "hbm", "achieved": round(p_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                              "frac": round(p_gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+                              "frac": round(p_gbs / PEAK_HBM_GBS, 4),
+                              "traffic": load_traffic("decode_paged+lse_merge_kernel")}}
         del kp, vp
 
     varlen = None
@@ -287,8 +329,7 @@ def main():
             ov = torch.empty_like(qv)
             lv = torch.empty(qv.shape[:2], dtype=torch.float32, device=dev)
             mq = max(lq)
-            for _ in range(10):
-                fa.fa_fwd_varlen(qv, kv_, vv, cq, ck, mq, causal=True, out=ov, lse=lv)
+            warm(lambda: fa.fa_fwd_varlen(qv, kv_, vv, cq, ck, mq, causal=True, out=ov, lse=lv))
             vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(args.varlen_steps)]
             torch.cuda.synchronize()
@@ -304,7 +345,8 @@ def main():
                 "value": round(v_tf, 2), "unit": "TFLOP/s", "avg_call_ms": round(v_ms, 5), "flop_per_call": v_flop,
                 "workload": f"fa_fwd_varlen Hq=32 Hkv=8 d=128 causal bf16, key lengths {lens}, query lengths {lq}",
                 "roofline": {"bound": "mfma", "achieved": round(v_tf, 2), "peak": PEAK_BF16_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(v_tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+                             "unit": "TFLOP/s", "frac": round(v_tf / PEAK_BF16_TFLOPS, 4),
+                             "traffic": load_traffic("fwd_bf16_pp_kernel_packed") if name == "packed" else None}}
             print(f"[bench] varlen {name}: {v_ms:.3f} ms, {v_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
             del qv, kv_, vv, ov, lv
 
@@ -313,8 +355,7 @@ def main():
         # The long-context prefill on E4M3 inputs (per-tensor quantised).
         q8, k8, v8, _, ds8 = inputs.make_fp8_inputs(3, "e4m3")
         q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
-        for _ in range(10):
-            fa.fa_fwd_fp8(q8, k8, v8, *ds8, causal=True, out=o3, lse=l3)
+        warm(lambda: fa.fa_fwd_fp8(q8, k8, v8, *ds8, causal=True, out=o3, lse=l3))
         fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.fp8_steps)]
         torch.cuda.synchronize()
@@ -332,7 +373,8 @@ def main():
                             "peak": round(PEAK_FP8_BF16_MIX_TFLOPS, 1), "unit": "TFLOP/s",
                             "peak_note": "Q.K^T at the FP8 peak (5033 TFLOP/s), P.V at the bf16 peak (2517)",
                             "frac": round(f8_tf / PEAK_FP8_BF16_MIX_TFLOPS, 4),
-                            "frac_of_fp8_peak": round(f8_tf / PEAK_FP8_TFLOPS, 4), "traffic": None}}
+                            "frac_of_fp8_peak": round(f8_tf / PEAK_FP8_TFLOPS, 4),
+                            "traffic": load_traffic("fwd_fp8_pp_kernel")}}
         print(f"[bench] fp8 prefill: {f8_ms:.3f} ms, {f8_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
         del q8, k8, v8
 

@@ -56,6 +56,14 @@ struct Fp8Tile {
 // bank groups of a 256-byte LDS line exactly once.
 __device__ __forceinline__ int swz_k8(int r) { return (r >> 1) & 7; }
 
+// Swizzle of the converted bf16 V tiles: the bf16 kernel's swz_v128 (which
+// keeps the transposed fragment reads conflict-free) plus a swap of the two
+// chunks of each pair in odd rows.  The staging writes store chunk pairs
+// (2j, 2j+1) of two adjacent rows in one instruction; with the swap the two
+// rows' first chunks fall in different bank halves.  Reads are unaffected:
+// the swap stays inside each aligned group of four chunks they touch.
+__device__ __forceinline__ int swz_v8(int r) { return 4 * (r & 3) + (r & 1); }
+
 template <int FMT>
 __device__ __forceinline__ f32x16 mfma32x32x64_f8(i32x8 a, i32x8 b, f32x16 c) {
   // FMT selects the operand format of both A and B: 0 = E4M3, 1 = E5M2.
@@ -149,8 +157,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     copy16_to_lds(kg + (size_t)k0 * D, voff, lds + buf * T::KTILE + wave_u * 1024);
   };
   // V staging: thread (w, i) loads 16 codes of row 8w + i/8 (columns
-  // 16*(i%8) .. +15), converts them to bf16 and writes two 16-byte chunks of
-  // the bf16 row, swizzled as the bf16 kernel's V tiles (swz_v128).
+  // 16*(i%8) .. +15), converts them to bf16 and writes the two 16-byte
+  // chunks 2*(i%8), 2*(i%8)+1 of the bf16 row (swizzled by swz_v8).
   uint4 vstage;
   auto load_v = [&](int t) {
     t = min(t, n_kt - 1);
@@ -168,10 +176,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     hi4.y = fp8x2_to_bf16x2<FMT, true>(vstage.z);
     hi4.z = fp8x2_to_bf16x2<FMT, false>(vstage.w);
     hi4.w = fp8x2_to_bf16x2<FMT, true>(vstage.w);
-    const int pos = (2 * st_chunk) ^ swz_v128(st_row);  // even: the pair stays adjacent
+    const int pos = (2 * st_chunk) ^ swz_v8(st_row);  // chunk 2j; chunk 2j+1 sits at pos ^ 1
     uint16_t* vrow = (uint16_t*)(lds + T::V_BASE) + buf * T::VTILE + st_row * D;
     *(uint4*)(vrow + pos * 8) = lo;
-    *(uint4*)(vrow + pos * 8 + 8) = hi4;
+    *(uint4*)(vrow + (pos ^ 1) * 8) = hi4;
   };
 
   // Per-lane fragment offsets.  K (bytes): row kb*32 + li, chunks 4s + 2hi
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int v_off[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
-    v_off[db] = tr_r * D + (((4 * db + tr_cc) ^ swz_v128(tr_r)) * 8) + tr_in;
+    v_off[db] = tr_r * D + (((4 * db + tr_cc) ^ swz_v8(tr_r)) * 8) + tr_in;
 #pragma unroll
   for (int st = 0; st < 2; ++st)
 #pragma unroll
