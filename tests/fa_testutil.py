@@ -49,7 +49,8 @@ def compare(o, lse, O_ref, L_ref, dtype, what="", o_tol=None, l_tol=None):
     fin = sel & ~ninf_ref
     do = np.abs(o64 - O_ref)
     do[~fin] = 0.0
-    dl = np.abs(np.where(fin, l64 - L_ref, 0.0))
+    with np.errstate(invalid="ignore"):  # -inf - -inf on rows outside `fin`
+        dl = np.abs(np.where(fin, l64 - L_ref, 0.0))
     eo, el = float(do.max(initial=0.0)), float(dl.max(initial=0.0))
     if eo > 0:
         idx = np.unravel_index(int(np.argmax(do)), do.shape)
