@@ -405,22 +405,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // (l % 16) ^ swizzle(row), to LDS position l % 16 (K: swz, V: swz_v128).
   // Tiles past the last one are clamped to it: the copy then lands in a
   // buffer no phase reads, which keeps exactly four copies per step.
+  // The lane offsets of a full tile's copies are the same for every tile:
+  // computed once here (bytes; the first copy's carries the +1 KiB bias of
+  // copy16x2_to_lds).  Only the last tile of a sequence, where rows past the
+  // length re-read the last valid row, adjusts them.
+  static_assert(T::COPIES == 2, "copies are issued in pairs");
+  const int cp_r0 = (wave_u * T::COPIES) * T::RPI + (lane >> 4), cp_r1 = cp_r0 + T::RPI;
+  int cp_k0 = (cp_r0 * D + (((lane & 15) ^ swz<D>(cp_r0)) * 8)) * 2 + 1024;
+  int cp_k1 = (cp_r1 * D + (((lane & 15) ^ swz<D>(cp_r1)) * 8)) * 2;
+  int cp_v0 = (cp_r0 * D + (((lane & 15) ^ swz_v128(cp_r0)) * 8)) * 2 + 1024;
+  int cp_v1 = (cp_r1 * D + (((lane & 15) ^ swz_v128(cp_r1)) * 8)) * 2;
+  asm volatile("" : "+v"(cp_k0), "+v"(cp_k1), "+v"(cp_v0), "+v"(cp_v1));
   auto copy_tile = [&](const uint16_t* src, int t, uint16_t* dst, bool is_v) {
     t = min(t, n_kt - 1);
     const int k0 = t * BN;
     const uint16_t* base = src + (size_t)k0 * D;
-    const bool tail = k0 + BN > kv_len;  // rows past the length re-read the last valid row
-    int voff[T::COPIES];
-#pragma unroll
-    for (int i = 0; i < T::COPIES; ++i) {
-      const int r = (wave_u * T::COPIES + i) * T::RPI + (lane >> 4);
-      const int chunk = (lane & 15) ^ (is_v ? swz_v128(r) : swz<D>(r));
-      const int row = tail ? min(k0 + r, kv_len - 1) - k0 : r;
-      voff[i] = (row * D + chunk * 8) * 2;
+    int o0 = is_v ? cp_v0 : cp_k0, o1 = is_v ? cp_v1 : cp_k1;
+    if (k0 + BN > kv_len) {  // rows past the length re-read the last valid row
+      o0 -= max(0, k0 + cp_r0 - (kv_len - 1)) * (2 * D);
+      o1 -= max(0, k0 + cp_r1 - (kv_len - 1)) * (2 * D);
     }
     // the wave's two copies are adjacent in LDS: one m0 setting serves both
-    static_assert(T::COPIES == 2, "copies are issued in pairs");
-    copy16x2_to_lds((const char*)base - 1024, voff[0] + 1024, voff[1], dst + wave_u * T::COPIES * 512);
+    copy16x2_to_lds((const char*)base - 1024, o0, o1, dst + wave_u * T::COPIES * 512);
   };
 
   int k_off[D / 16];
@@ -586,8 +592,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // A work-group with no visible tile (empty sequence, or every row above
   // the causal diagonal) runs no step: its copies would address tile -1.
   if (n_kt > 0) {
-    for (int j = 0; j <= n_kt; ++j) {
-      const int b0 = j % 3, b1 = (j + 1) % 3, b2 = (j + 2) % 3;
+    // Step j uses buffers j % 3 (K_j), (j + 2) % 3 (V_{j-1}, then K_{j+2})
+    // and (j + 1) % 3 (V_{j+1}).  The loop is unrolled by three so that every
+    // buffer index is a constant and the buffer bases fold into the LDS
+    // instructions' offset fields.
+    auto step = [&](int j, int b0, int b1, int b2) {
       matrix_phase(b0, b2);  // K_j in K buffer b0, V_{j-1} in V buffer b2
       // Copies go out after the matrix work is issued: at the start of the
       // phase all four waves of the group would queue them at once, holding
@@ -599,6 +608,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       softmax_phase(j);
       wait_copies();
       barrier();
+    };
+    for (int j = 0; j <= n_kt; j += 3) {
+      step(j, 0, 1, 2);
+      if (j + 1 > n_kt) break;
+      step(j + 1, 1, 2, 0);
+      if (j + 2 > n_kt) break;
+      step(j + 2, 2, 0, 1);
     }
   }
   if (lead) barrier();

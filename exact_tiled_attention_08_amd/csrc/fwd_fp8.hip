@@ -147,13 +147,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // global_load_lds_dwordx4); lane i brings row 8w + i/8, source chunk
   // (i % 8) ^ swz_k8(row), to LDS position i % 8 of that row.  Tiles past the
   // last one are clamped to it (the copy lands in a buffer no phase reads).
+  // The lane offsets are the same for every full tile (computed once); only
+  // the last tile of a sequence, where rows past the length re-read the last
+  // valid row, adjusts them.
   const int st_row = wave_u * 8 + (lane >> 3);
   const int st_chunk = lane & 7;
+  int k_cp = st_row * D + ((st_chunk ^ swz_k8(st_row)) << 4);
+  int v_ld = st_row * D + st_chunk * 16;
+  asm volatile("" : "+v"(k_cp), "+v"(v_ld));
+  // rows by which a lane's row moves back in the last tile (0 elsewhere)
+  auto tail_shift = [&](int k0) { return (k0 + BN > kv_len) ? max(0, k0 + st_row - (kv_len - 1)) : 0; };
   auto copy_k = [&](int t, int buf) {
     t = min(t, n_kt - 1);
     const int k0 = t * BN;
-    const int row = (k0 + BN > kv_len) ? min(k0 + st_row, kv_len - 1) - k0 : st_row;
-    const int voff = row * D + ((st_chunk ^ swz_k8(st_row)) << 4);
+    int voff = k_cp;
+    if (k0 + BN > kv_len) voff -= tail_shift(k0) * D;
     copy16_to_lds(kg + (size_t)k0 * D, voff, lds + buf * T::KTILE + wave_u * 1024);
   };
   // V staging: thread (w, i) loads 16 codes of row 8w + i/8 (columns
@@ -163,8 +171,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto load_v = [&](int t) {
     t = min(t, n_kt - 1);
     const int k0 = t * BN;
-    const int row = (k0 + BN > kv_len) ? min(k0 + st_row, kv_len - 1) : k0 + st_row;
-    vstage = *(const uint4*)(vg + (size_t)row * D + st_chunk * 16);
+    int off = v_ld;
+    if (k0 + BN > kv_len) off -= tail_shift(k0) * D;
+    vstage = *(const uint4*)(vg + (size_t)k0 * D + off);
   };
   auto store_v = [&](int buf) {
     uint4 lo, hi4;
@@ -341,8 +350,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   barrier();
   if (!lead) barrier();
   if (n_kt > 0) {
-    int b0 = 0, b1 = 1, b2 = 2;  // j % 3, (j + 1) % 3, (j + 2) % 3
-    for (int j = 0; j <= n_kt; ++j) {
+    // Step j uses buffers b0 = j % 3, b1 = (j + 1) % 3, b2 = (j + 2) % 3; the
+    // loop is unrolled by three so that they are constants.
+    auto step = [&](int j, int b0, int b1, int b2) {
       matrix_phase(b0, b2);  // K_j in K buffer b0, V_{j-1} in V buffer b2
       copy_k(j + 2, b2);
       wait_copies();
@@ -352,11 +362,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       load_v(j + 2);
       wait_copies();
       barrier();
-      const int t = b0;
-      b0 = b1;
-      b1 = b2;
-      b2 = t;
-      asm volatile("" : "+s"(b0), "+s"(b1), "+s"(b2));
+    };
+    for (int j = 0; j <= n_kt; j += 3) {
+      step(j, 0, 1, 2);
+      if (j + 1 > n_kt) break;
+      step(j + 1, 1, 2, 0);
+      if (j + 2 > n_kt) break;
+      step(j + 2, 2, 0, 1);
     }
   }
   if (lead) barrier();
