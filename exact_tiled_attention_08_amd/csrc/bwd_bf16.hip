@@ -9,13 +9,14 @@
 //     dP_ij = dO_i . V_j
 //     dS_ij = P_ij (dP_ij - D_i),   D_i = dO_i . O_i
 //     dV_j += P_ij dO_i,   dK_j += scale dS_ij Q_i,   dQ_i += scale dS_ij K_j
-// Three kernels: D (one dot product per query row), dQ (one work-group per
-// 128-query block streaming 32-key tiles), and dK/dV (one work-group per
+// Four launches: D (one dot product per query row), dQ (one work-group per
+// 128-query block streaming 32-key tiles), then dV and dK (one work-group per
 // 128-key block streaming the 32-query tiles of every query head that reads
-// it).  The two gradient kernels keep different operands on the lanes -- dQ
-// the queries (as in the forward), dK/dV the keys -- so every product takes
-// its operands straight from the recomputed tiles: no atomics and no extra
-// transposes beyond the ds_read_b64_tr_b16 reads already used by the forward.
+// it; one kernel, two parts).  The gradient kernels keep different operands
+// on the lanes -- dQ the queries (as in the forward), dV/dK the keys -- so
+// every product takes its operands straight from the recomputed tiles: no
+// atomics and no extra transposes beyond the ds_read_b64_tr_b16 reads already
+// used by the forward.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -223,17 +224,23 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: 4 waves x 32 keys per work-group (the block's K and V stay in LDS);
-// 32-query tiles of every query head that reads this KV head.  Per tile and
-// wave, with the keys on the lanes:
-//   S  = Q K^T,  dP = dO V^T                (A: Q / dO rows, B: K / V rows, all from LDS)
-//   dS = P * (dP - D)                       (P recomputed from the LSE)
-//   dV^T += dO^T P,  dK^T += Q^T dS         (A: transposed reads of dO / Q, B: P / dS)
-template <int D, bool CAUSAL, bool PADDED>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
+// dV and dK, in two launches of one kernel (PART = 0: dV, PART = 1: dK): 4
+// waves x 32 keys per work-group; 32-query tiles of every query head that
+// reads this KV head.  Per tile and wave, with the keys on the lanes:
+//   S  = Q K^T                  (A: Q rows from LDS, B: K rows)          both parts
+//   P  = 2^(S scale log2(e) - LSE)                                        both parts
+//   dV^T += dO^T P              (A: transposed reads of dO, B: P)         PART 0
+//   dP = dO V^T,  dS = P * (dP - D)
+//   dK^T += Q^T dS              (A: transposed reads of Q, B: dS)         PART 1
+// Splitting the two gradients costs one more product (S is recomputed by
+// both) but halves each launch's accumulators (64 registers), so two or more
+// work-groups share a CU instead of one.  PART 0 keeps the block's K rows in
+// LDS; PART 1 keeps each wave's K rows in registers and the block's V rows in
+// LDS.
+template <int D, bool CAUSAL, bool PADDED, int PART>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BK = 128, BQ = 32;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[BK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[BK * D];  // K (PART 0) or V (PART 1)
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[BQ * D];
   __shared__ __attribute__((aligned(16))) uint16_t do_lds[BQ * D];
   __shared__ __attribute__((aligned(16))) float lse_lds[BQ];
@@ -253,12 +260,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const size_t kv_base = ((size_t)b * p.Hkv + hk) * (size_t)p.Nk;
   const int key = kt0 + wave * 32 + li;  // this lane's key (both halves)
 
+  // PART 1: B operand of S from registers -- lane (li, hi) holds K of key
+  // `key`, columns 16*st + 8*hi .. +7 (zeros past the sequence's length).
+  bf16x8 kf[PART == 1 ? D / 16 : 1];
+  if constexpr (PART == 1) {
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st)
+      kf[st] = key < kv_len ? *(const bf16x8*)(p.k + (kv_base + key) * D + 16 * st + 8 * hi) : bf16x8{};
+  }
   {
-    TileStage<D, BK> kst, vst;
-    kst.load(p.k + (kv_base + kt0) * D, kv_len - kt0, tid);
-    vst.load(p.v + (kv_base + kt0) * D, kv_len - kt0, tid);
-    kst.store(k_lds, tid);
-    vst.store(v_lds, tid);
+    TileStage<D, BK> st_kv;
+    st_kv.load((PART == 0 ? p.k : p.v) + (kv_base + kt0) * D, kv_len - kt0, tid);
+    st_kv.store(kv_lds, tid);
   }
 
   // Query tiles that can see a key of this block: all of them, from the one
@@ -270,9 +283,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int per_head = kt0 < kv_len ? max(0, n_qt - qt_first) : 0;
   const int n_it = per_head * group;
 
-  f32x16 dk_acc[D / 32], dv_acc[D / 32];
+  f32x16 acc[D / 32];  // dV (PART 0) or dK (PART 1), transposed
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) dk_acc[db] = dv_acc[db] = f32x16{};
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
   TileStage<D, BQ> qst, dost;
   float lse_r = 0.f, d_r = 0.f;  // staged by threads 0 .. BQ-1
@@ -304,58 +317,54 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-      const int kr = wave * 32 + li;
-      s = mfma32x32x16(*(const bf16x8*)(q_lds + tile_off<D>(li, 2 * st + hi)),
-                       *(const bf16x8*)(k_lds + tile_off<D>(kr, 2 * st + hi)), s);
-      dp = mfma32x32x16(*(const bf16x8*)(do_lds + tile_off<D>(li, 2 * st + hi)),
-                        *(const bf16x8*)(v_lds + tile_off<D>(kr, 2 * st + hi)), dp);
+      const bf16x8 kb = PART == 1 ? kf[st] : *(const bf16x8*)(kv_lds + tile_off<D>(wave * 32 + li, 2 * st + hi));
+      s = mfma32x32x16(*(const bf16x8*)(q_lds + tile_off<D>(li, 2 * st + hi)), kb, s);
+      if constexpr (PART == 1)
+        dp = mfma32x32x16(*(const bf16x8*)(do_lds + tile_off<D>(li, 2 * st + hi)),
+                          *(const bf16x8*)(kv_lds + tile_off<D>(wave * 32 + li, 2 * st + hi)), dp);
     }
     // lane l: key `key`; register r: query q0 + 8(r/4) + 4*hi + r%4
-    float pr[16], ds[16];
+    float g[16];  // P (PART 0) or dS (PART 1)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float4 lv = *(const float4*)(lse_lds + 8 * j + 4 * hi);
-      const float4 dv4 = *(const float4*)(d_lds + 8 * j + 4 * hi);
-      const float lse4[4] = {lv.x, lv.y, lv.z, lv.w}, d4[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+      const float lse4[4] = {lv.x, lv.y, lv.z, lv.w};
+      float d4[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (PART == 1) {
+        const float4 dv4 = *(const float4*)(d_lds + 8 * j + 4 * hi);
+        d4[0] = dv4.x; d4[1] = dv4.y; d4[2] = dv4.z; d4[3] = dv4.w;
+      }
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int r = 4 * j + x;
         const int q = q0 + 8 * j + 4 * hi + x;
         bool vis = key < kv_len && q < p.Nq;
         if (CAUSAL) vis = vis && key <= q + diag;
-        pr[r] = vis ? fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -lse4[x])) : 0.f;
-        ds[r] = pr[r] * (dp[r] - d4[x]);
+        const float pr = vis ? fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -lse4[x])) : 0.f;
+        g[r] = PART == 0 ? pr : pr * (dp[r] - d4[x]);
       }
     }
-    bf16x8 pf[2], dsf[2];
+    bf16x8 gf[2];
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      pf[mm] = pack_bf16x8(pr + 8 * mm);
-      dsf[mm] = pack_bf16x8(ds + 8 * mm);
-    }
+    for (int mm = 0; mm < 2; ++mm) gf[mm] = pack_bf16x8(g + 8 * mm);
+    const uint16_t* a_tile = PART == 0 ? do_lds : q_lds;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        dv_acc[db] = mfma32x32x16(tr_fragment<D>(do_lds, 16 * mm, db, lane), pf[mm], dv_acc[db]);
-        dk_acc[db] = mfma32x32x16(tr_fragment<D>(q_lds, 16 * mm, db, lane), dsf[mm], dk_acc[db]);
-      }
+      for (int mm = 0; mm < 2; ++mm) acc[db] = mfma32x32x16(tr_fragment<D>(a_tile, 16 * mm, db, lane), gf[mm], acc[db]);
   }
 
   if (key < p.Nk) {
-    uint16_t* kp = p.dk + (kv_base + key) * D;
-    uint16_t* vp = p.dv + (kv_base + key) * D;
+    uint16_t* op = (PART == 0 ? p.dv : p.dk) + (kv_base + key) * D;
+    const float f = PART == 0 ? 1.f : p.scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint2 wk, wv;
-        wk.x = pack_bf16x2(dk_acc[db][4 * g] * p.scale, dk_acc[db][4 * g + 1] * p.scale);
-        wk.y = pack_bf16x2(dk_acc[db][4 * g + 2] * p.scale, dk_acc[db][4 * g + 3] * p.scale);
-        wv.x = pack_bf16x2(dv_acc[db][4 * g], dv_acc[db][4 * g + 1]);
-        wv.y = pack_bf16x2(dv_acc[db][4 * g + 2], dv_acc[db][4 * g + 3]);
-        *(uint2*)(kp + db * 32 + 8 * g + 4 * hi) = wk;
-        *(uint2*)(vp + db * 32 + 8 * g + 4 * hi) = wv;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        uint2 w;
+        w.x = pack_bf16x2(acc[db][4 * g4] * f, acc[db][4 * g4 + 1] * f);
+        w.y = pack_bf16x2(acc[db][4 * g4 + 2] * f, acc[db][4 * g4 + 3] * f);
+        *(uint2*)(op + db * 32 + 8 * g4 + 4 * hi) = w;
       }
   }
 }
@@ -388,8 +397,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   const long long krows = (long long)a.B * a.Hkv * a.Nk;
   if (krows > 0) {
     p.n_tiles = (a.Nk + 127) / 128;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, PADDED>), dim3((unsigned)((long long)p.n_tiles * a.B * a.Hkv)),
-                       dim3(256), 0, a.stream, p);
+    const dim3 grid((unsigned)((long long)p.n_tiles * a.B * a.Hkv));
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, PADDED, 0>), grid, dim3(256), 0, a.stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, PADDED, 1>), grid, dim3(256), 0, a.stream, p);
   }
   return hipGetLastError();
 }
