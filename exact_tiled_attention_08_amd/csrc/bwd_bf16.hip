@@ -122,13 +122,14 @@ __device__ __forceinline__ float lse_base2(float lse) { return lse == kNegInf ? 
 //   dS^T = P^T * (dP^T - D)                (P^T recomputed from the LSE)
 //   dQ^T += K^T dS^T                       (A: K^T by transposed reads, B: dS^T)
 template <int D, bool CAUSAL, bool PADDED>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BwdParams p) {
   constexpr int BM = 128, BN = 32;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[BN * D];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, li = lane & 31, hi = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int bh_count = p.B * p.Hq;
   const int bh = blockIdx.x % bh_count;
   const int qt = p.n_tiles - 1 - (int)(blockIdx.x / bh_count);  // heaviest (causal) first
@@ -190,15 +191,22 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
       s = mfma32x32x16(*(const bf16x8*)(k_lds + tile_off<D>(li, 2 * st + hi)), qf[st], s);
       dp = mfma32x32x16(*(const bf16x8*)(v_lds + tile_off<D>(li, 2 * st + hi)), dof[st], dp);
     }
-    // lane l: query qrow; register r: key k0 + 8(r/4) + 4*hi + r%4
+    // lane l: query qrow; register r: key k0 + 8(r/4) + 4*hi + r%4.  Tiles
+    // whose keys are all valid and visible to every row of the wave skip the
+    // per-element mask (rows past Nq have LSE +inf, so their P is 0 anyway).
     float ds[16];
+    if (k0 + BN <= kv_len && (!CAUSAL || k0 + BN - 1 <= q0 + wave_u * 32 + diag)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = k0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      bool vis = key < kv_len;
-      if (CAUSAL) vis = vis && key <= qrow + diag;
-      const float pr = vis ? fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -lse2)) : 0.f;
-      ds[r] = pr * (dp[r] - drow);
+      for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -lse2)) * (dp[r] - drow);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        bool vis = key < kv_len;
+        if (CAUSAL) vis = vis && key <= qrow + diag;
+        const float pr = vis ? fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -lse2)) : 0.f;
+        ds[r] = pr * (dp[r] - drow);
+      }
     }
     bf16x8 dsf[2];
 #pragma unroll
@@ -259,6 +267,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   const int diag = p.Nk - p.Nq;
   const size_t kv_base = ((size_t)b * p.Hkv + hk) * (size_t)p.Nk;
   const int key = kt0 + wave * 32 + li;  // this lane's key (both halves)
+  const int key_end = kt0 + __builtin_amdgcn_readfirstlane(wave) * 32 + 32;  // past this wave's keys
 
   // PART 1: B operand of S from registers -- lane (li, hi) holds K of key
   // `key`, columns 16*st + 8*hi .. +7 (zeros past the sequence's length).
@@ -324,26 +333,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
                           *(const bf16x8*)(kv_lds + tile_off<D>(wave * 32 + li, 2 * st + hi)), dp);
     }
     // lane l: key `key`; register r: query q0 + 8(r/4) + 4*hi + r%4
+    // Tiles whose queries all see every key of the wave skip the per-element
+    // mask (query rows past Nq have LSE +inf, so their P is 0 anyway).
+    const bool full = key_end <= kv_len && (!CAUSAL || key_end - 1 <= q0 + diag);
     float g[16];  // P (PART 0) or dS (PART 1)
+    auto tile_elems = [&](bool masked) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 lv = *(const float4*)(lse_lds + 8 * j + 4 * hi);
-      const float lse4[4] = {lv.x, lv.y, lv.z, lv.w};
-      float d4[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (PART == 1) {
-        const float4 dv4 = *(const float4*)(d_lds + 8 * j + 4 * hi);
-        d4[0] = dv4.x; d4[1] = dv4.y; d4[2] = dv4.z; d4[3] = dv4.w;
-      }
+      for (int j = 0; j < 4; ++j) {
+        const float4 lv = *(const float4*)(lse_lds + 8 * j + 4 * hi);
+        const float lse4[4] = {lv.x, lv.y, lv.z, lv.w};
+        float d4[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (PART == 1) {
+          const float4 dv4 = *(const float4*)(d_lds + 8 * j + 4 * hi);
+          d4[0] = dv4.x; d4[1] = dv4.y; d4[2] = dv4.z; d4[3] = dv4.w;
+        }
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int r = 4 * j + x;
-        const int q = q0 + 8 * j + 4 * hi + x;
-        bool vis = key < kv_len && q < p.Nq;
-        if (CAUSAL) vis = vis && key <= q + diag;
-        const float pr = vis ? fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -lse4[x])) : 0.f;
-        g[r] = PART == 0 ? pr : pr * (dp[r] - d4[x]);
+        for (int x = 0; x < 4; ++x) {
+          const int r = 4 * j + x;
+          const int q = q0 + 8 * j + 4 * hi + x;
+          bool vis = true;
+          if (masked) {
+            vis = key < kv_len && q < p.Nq;
+            if (CAUSAL) vis = vis && key <= q + diag;
+          }
+          const float pr = vis ? fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -lse4[x])) : 0.f;
+          g[r] = PART == 0 ? pr : pr * (dp[r] - d4[x]);
+        }
       }
-    }
+    };
+    if (full) tile_elems(false);
+    else tile_elems(true);
     bf16x8 gf[2];
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm) gf[mm] = pack_bf16x8(g + 8 * mm);
