@@ -277,12 +277,13 @@ def main():
         bwd = {"value": round(bwd_tf, 2), "unit": "TFLOP/s",
                "workload": "backward of prefill B=1 H=32 N=8192 d=128 causal bf16 (dQ, dK, dV)",
                "flop_per_call": f_bwd, "flop_count": "5 products of 2*d FLOP per visible (query, key) pair: "
-                                                     "S recomputed, dP, dV, dK, dQ (2.5x the forward)",
+                                                     "S recomputed, dP, dV, dK, dQ (2.5x the forward); the "
+                                                     "kernels execute 8 (S in all three, dP in two)",
                "avg_call_ms": round(bwd_ms, 5),
-               "roofline": {"bound": "mfma", "kernel": "bwd_rowdot + bwd_dq_kernel + bwd_dkdv_kernel",
+               "roofline": {"bound": "mfma", "kernel": "bwd_rowdot + bwd_dq_kernel + bwd_dkdv_kernel<dV> + <dK>",
                             "achieved": round(bwd_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
-                            "traffic": load_traffic("bwd_rowdot+bwd_dq+bwd_dkdv")}}
+                            "traffic": load_traffic("bwd_rowdot+bwd_dq+bwd_dv+bwd_dk")}}
 
     paged = None
     if args.paged_steps > 0:
