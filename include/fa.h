@@ -34,7 +34,9 @@
  *  - q, k, v, o and the partials must be 16-byte aligned; lse 4-byte aligned.
  *  - stream is a hipStream_t (NULL = the null stream).  Calls enqueue work and
  *    return without synchronising.  Arguments are validated on the host before
- *    any HIP call; a device fault surfaces at the caller's next sync.
+ *    any HIP call; a device fault surfaces at the caller's next sync.  A call
+ *    launches kernels only (no allocation, memset or synchronisation), so it
+ *    may be captured in a HIP graph and replayed.
  *  - Every call returns an fa_status; on failure fa_last_error() gives a
  *    thread-local message.
  *  - Sizes may be zero: a call with no output elements returns FA_OK without
