@@ -15,7 +15,7 @@ from ._lib import FAError, FA_DECODE_SPLIT_ALIGN, FA_MAX_SPLITS  # noqa: F401
 
 __all__ = ["fa_fwd", "fa_fwd_fp8", "fa_fwd_varlen", "fa_decode_splitkv", "fa_lse_merge", "fa_decode", "fa_decode_workspace_bytes",
            "fa_decode_paged", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_last_error", "FAError",
-           "default_scale"]
+           "default_scale", "attention"]
 
 _DTYPES = {torch.bfloat16: _lib.FA_BF16, torch.float32: _lib.FA_F32}
 
@@ -329,6 +329,36 @@ def fa_bwd(q, k, v, o, lse, dout, causal=False, kv_seqlens=None, scale=None, wor
                           _ptr(dv), B, Hq, Hkv, Nq, Nk, d, s, int(bool(causal)), _ptr(lens), _ptr(workspace),
                           workspace.numel(), _lib.FA_BF16, _stream(q)))
     return dq, dk, dv
+
+
+class _Attention(torch.autograd.Function):
+    """fa_fwd in the forward pass, fa_bwd in the backward pass (bf16)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal, kv_seqlens, scale):
+        o, lse = fa_fwd(q, k, v, causal=causal, kv_seqlens=kv_seqlens, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse, kv_seqlens)
+        ctx.causal, ctx.scale = causal, scale
+        ctx.mark_non_differentiable(lse)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, do, _dlse):
+        q, k, v, o, lse, kv_seqlens = ctx.saved_tensors
+        dq, dk, dv = fa_bwd(q, k, v, o, lse, do.contiguous(), causal=ctx.causal, kv_seqlens=kv_seqlens,
+                            scale=ctx.scale)
+        return dq, dk, dv, None, None, None
+
+
+def attention(q, k, v, causal=False, kv_seqlens=None, scale=None):
+    """Exact attention with autograd: returns O (bf16 [B, Hq, Nq, d]) and keeps what
+    fa_bwd needs for the backward pass.  q [B, Hq, Nq, d], k/v [B, Hkv, Nk, d] in
+    bf16; kv_seqlens and scale as in fa_fwd.  The LSE is not returned: gradients
+    flow through O only."""
+    if q.dtype != torch.bfloat16:
+        raise ValueError("attention() with gradients takes bf16 inputs (the backward pass is bf16 only)")
+    o, _ = _Attention.apply(q, k, v, bool(causal), kv_seqlens, scale)
+    return o
 
 
 def fa_status_string(status):
