@@ -43,7 +43,8 @@ def kernel_source_hash():
 def prefill_flops(B, H, Nq, Nk, d, causal):
     """4*d FLOP per allowed (query, key) pair."""
     if causal:
-        pairs = sum(min(Nk, i + (Nk - Nq) + 1) for i in range(Nq)) if Nq != Nk else Nq * (Nq + 1) // 2
+        pairs = (sum(max(0, min(Nk, i + (Nk - Nq) + 1)) for i in range(Nq)) if Nq != Nk
+                 else Nq * (Nq + 1) // 2)
     else:
         pairs = Nq * Nk
     return 4.0 * d * B * H * pairs
