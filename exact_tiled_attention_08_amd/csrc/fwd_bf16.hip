@@ -481,27 +481,36 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   // Positions 0..3 of the pipeline run the P.V groups (G4..G7) and positions
   // 4..7 the S groups (G0..G3): P_{j-1} is dead before S_j comes alive.
-  auto run_groups = [&](int i0, int i1) {
+  // The first two groups of a matrix phase (both P.V, reading V_{j-1}) are
+  // loaded at the start of the wave's previous softmax phase, so the phase
+  // opens with MFMAs instead of waiting on LDS.  That is safe: V_{j-1} was
+  // copied two steps back and the barrier opening that softmax phase comes
+  // after every wave's wait for those copies; no copy in flight then targets
+  // its buffer.
+  constexpr int PRE = 2;
+  bf16x8 fa[4], fb[4];
+  auto run_groups = [&]() {
     auto grp = [](int i) { return i < 4 ? i + 4 : i - 4; };
-    bf16x8 fa[4], fb[4];
-    load_group(grp(i0), fa);
 #pragma unroll
-    for (int i = i0; i < i1; ++i) {
-      if (i + 1 < i1) load_group(grp(i + 1), ((i - i0) & 1) ? fa : fb);
-      mfma_group(grp(i), ((i - i0) & 1) ? fb : fa);
+    for (int i = 0; i < 8; ++i) {
+      if (i + 1 < 8 && i + 1 >= PRE) load_group(grp(i + 1), (i & 1) ? fa : fb);
+      mfma_group(grp(i), (i & 1) ? fb : fa);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  auto preload = [&]() {
+    load_group(4, fa);
+    load_group(5, fb);
   };
   // Every step runs all eight groups -- one code path keeps the register
   // allocation tight.  Work a wave does not need is harmless: S_j of a tile
   // past the wave's range is never used, and P.V runs with P = 0 (at j = 0,
   // and after a skipped softmax) against finite V data.
-  auto matrix_phase = [&](int kbuf, int vbuf) {
+  auto set_bufs = [&](int kbuf, int vbuf) {
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) ka[st] = k_off[st] + kbuf * T::TILE;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) va[db] = v_off[db] + vbuf * T::TILE;
-    run_groups(0, 8);
   };
 
   // Online-softmax update for tile j (S_j -> P_j), as in the 4-wave kernel.
@@ -597,7 +606,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // buffer index is a constant and the buffer bases fold into the LDS
     // instructions' offset fields.
     auto step = [&](int j, int b0, int b1, int b2) {
-      matrix_phase(b0, b2);  // K_j in K buffer b0, V_{j-1} in V buffer b2
+      run_groups();  // K_j in K buffer b0, V_{j-1} in V buffer b2 (set and preloaded before)
       // Copies go out after the matrix work is issued: at the start of the
       // phase all four waves of the group would queue them at once, holding
       // back their first MFMAs.
@@ -605,10 +614,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       copy_tile(vg, j + 1, kv_lds[3 + b1], true);
       wait_copies();
       barrier();
+      set_bufs(b1, b0);  // step j + 1: K_{j+1} in K buffer b1, V_j in V buffer b0
+      preload();         // (after the last step: harmless reads that nothing uses)
       softmax_phase(j);
       wait_copies();
       barrier();
     };
+    set_bufs(0, 2);
+    preload();
     for (int j = 0; j <= n_kt; j += 3) {
       step(j, 0, 1, 2);
       if (j + 1 > n_kt) break;
