@@ -81,8 +81,9 @@ def fa_fwd(q, k, v, causal=False, kv_seqlens=None, scale=None, out=None, lse=Non
         raise ValueError("out/lse have the wrong shape")
     s = default_scale(d) if scale is None else float(scale)
     lib = _lib.load()
-    _lib.check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, s,
-                          int(bool(causal)), _ptr(lens), _DTYPES[q.dtype], _stream(q)))
+    with torch.cuda.device(q.device):  # kernels launch on the current device
+        _lib.check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, s,
+                              int(bool(causal)), _ptr(lens), _DTYPES[q.dtype], _stream(q)))
     return out, lse
 
 
@@ -117,9 +118,10 @@ def fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False, kv_seqlen
         raise ValueError("out/lse have the wrong shape")
     s = default_scale(d) if scale is None else float(scale)
     lib = _lib.load()
-    _lib.check(lib.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, s,
-                              int(bool(causal)), _ptr(lens), float(q_descale), float(k_descale), float(v_descale),
-                              _FP8[q.dtype], _stream(q)))
+    with torch.cuda.device(q.device):  # kernels launch on the current device
+        _lib.check(lib.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, s,
+                                  int(bool(causal)), _ptr(lens), float(q_descale), float(k_descale), float(v_descale),
+                                  _FP8[q.dtype], _stream(q)))
     return out, lse
 
 
@@ -156,9 +158,10 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=Fals
         raise ValueError("out/lse have the wrong shape")
     s = default_scale(d) if scale is None else float(scale)
     lib = _lib.load()
-    _lib.check(lib.fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
-                                 _ptr(cu_seqlens_k), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), d, s,
-                                 int(bool(causal)), _DTYPES[q.dtype], _stream(q)))
+    with torch.cuda.device(q.device):  # kernels launch on the current device
+        _lib.check(lib.fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                                     _ptr(cu_seqlens_k), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), d, s,
+                                     int(bool(causal)), _DTYPES[q.dtype], _stream(q)))
     return out, lse
 
 
@@ -196,9 +199,10 @@ def fa_decode_splitkv(q, k_cache, v_cache, num_splits=16, kv_seqlens=None, scale
         raise ValueError("o_part/lse_part have the wrong shape")
     s = default_scale(d) if scale is None else float(scale)
     lib = _lib.load()
-    _lib.check(lib.fa_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o_part), _ptr(lse_part),
-                                     B, Hq, Hkv, Nk, d, s, _ptr(lens), num_splits, _DTYPES[q.dtype],
-                                     _stream(q)))
+    with torch.cuda.device(q.device):  # kernels launch on the current device
+        _lib.check(lib.fa_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o_part), _ptr(lse_part),
+                                         B, Hq, Hkv, Nk, d, s, _ptr(lens), num_splits, _DTYPES[q.dtype],
+                                         _stream(q)))
     return o_part, lse_part
 
 
@@ -222,8 +226,9 @@ def fa_lse_merge(o_part, lse_part, dtype=torch.bfloat16, out=None, lse=None):
     if out.numel() != rows * d or lse.numel() != rows:
         raise ValueError("out/lse have the wrong size")
     lib = _lib.load()
-    _lib.check(lib.fa_lse_merge(_ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse), rows, d, S,
-                                _DTYPES[dtype], _stream(o_part)))
+    with torch.cuda.device(o_part.device):  # kernels launch on the current device
+        _lib.check(lib.fa_lse_merge(_ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse), rows, d, S,
+                                    _DTYPES[dtype], _stream(o_part)))
     return out, lse
 
 
@@ -247,9 +252,10 @@ def fa_decode(q, k_cache, v_cache, kv_seqlens=None, num_splits=16, scale=None, w
     _check_tensor(out, "out", q.dtype, 4, q.device)
     _check_tensor(lse, "lse", torch.float32, 3, q.device)
     s = default_scale(d) if scale is None else float(scale)
-    _lib.check(lib.fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, Hq, Hkv, Nk, d,
-                             s, _ptr(lens), num_splits, _ptr(workspace), workspace.numel(),
-                             _DTYPES[q.dtype], _stream(q)))
+    with torch.cuda.device(q.device):  # kernels launch on the current device
+        _lib.check(lib.fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, Hq, Hkv, Nk, d,
+                                 s, _ptr(lens), num_splits, _ptr(workspace), workspace.numel(),
+                                 _DTYPES[q.dtype], _stream(q)))
     return out, lse
 
 
@@ -285,9 +291,10 @@ def fa_decode_paged(q, k_pages, v_pages, block_table, kv_seqlens, num_splits=16,
     _check_tensor(out, "out", q.dtype, 4, q.device)
     _check_tensor(lse, "lse", torch.float32, 3, q.device)
     s = default_scale(d) if scale is None else float(scale)
-    _lib.check(lib.fa_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(out), _ptr(lse),
-                                   B, Hq, Hkv, num_pages, page_size, block_table.shape[1], d, s, _ptr(lens),
-                                   num_splits, _ptr(workspace), workspace.numel(), _lib.FA_BF16, _stream(q)))
+    with torch.cuda.device(q.device):  # kernels launch on the current device
+        _lib.check(lib.fa_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(out), _ptr(lse),
+                                       B, Hq, Hkv, num_pages, page_size, block_table.shape[1], d, s, _ptr(lens),
+                                       num_splits, _ptr(workspace), workspace.numel(), _lib.FA_BF16, _stream(q)))
     return out, lse
 
 
@@ -325,9 +332,10 @@ def fa_bwd(q, k, v, o, lse, dout, causal=False, kv_seqlens=None, scale=None, wor
         if tuple(t.shape) != tuple(ref.shape):
             raise ValueError(f"{name} has the wrong shape")
     s = default_scale(d) if scale is None else float(scale)
-    _lib.check(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
-                          _ptr(dv), B, Hq, Hkv, Nq, Nk, d, s, int(bool(causal)), _ptr(lens), _ptr(workspace),
-                          workspace.numel(), _lib.FA_BF16, _stream(q)))
+    with torch.cuda.device(q.device):  # kernels launch on the current device
+        _lib.check(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                              _ptr(dv), B, Hq, Hkv, Nq, Nk, d, s, int(bool(causal)), _ptr(lens), _ptr(workspace),
+                              workspace.numel(), _lib.FA_BF16, _stream(q)))
     return dq, dk, dv
 
 
