@@ -479,18 +479,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32x32x16(f[db], pf[g - 4], oacc[db]);
     }
   };
-  // Positions 0..3 of the pipeline run the P.V groups (G4..G7) and positions
-  // 4..7 the S groups (G0..G3): P_{j-1} is dead before S_j comes alive.
-  // The first two groups of a matrix phase (both P.V, reading V_{j-1}) are
+  // The pipeline alternates P.V groups (G4..G7) and S groups (G0..G3): the
+  // P.V groups' transposed V reads move half the bytes per LDS cycle of the
+  // S groups' K reads, and alternating the two spreads the LDS demand evenly
+  // over the phase (+1 %, at the cost of P_{j-1} and S_j being live together).
+  // The first two groups of a matrix phase (P.V on V_{j-1}, S on K_j) are
   // loaded at the start of the wave's previous softmax phase, so the phase
-  // opens with MFMAs instead of waiting on LDS.  That is safe: V_{j-1} was
+  // opens with MFMAs instead of waiting on LDS.  That is safe: both tiles were
   // copied two steps back and the barrier opening that softmax phase comes
   // after every wave's wait for those copies; no copy in flight then targets
-  // its buffer.
+  // their buffers.
   constexpr int PRE = 2;
   bf16x8 fa[4], fb[4];
   auto run_groups = [&]() {
-    auto grp = [](int i) { return i < 4 ? i + 4 : i - 4; };
+    auto grp = [](int i) { return (i & 1) ? (i >> 1) : 4 + (i >> 1); };
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (i + 1 < 8 && i + 1 >= PRE) load_group(grp(i + 1), (i & 1) ? fa : fb);
@@ -500,7 +502,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   auto preload = [&]() {
     load_group(4, fa);
-    load_group(5, fb);
+    load_group(0, fb);
   };
   // Every step runs all eight groups -- one code path keeps the register
   // allocation tight.  Work a wave does not need is harmless: S_j of a tile
