@@ -65,6 +65,7 @@ def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Nq=16, Nk=16, d=64, sc
     (dict(Hkv=0), UNSUP), (dict(B=-1), BAD), (dict(Nk=-5), BAD), (dict(scale=0.0), BAD),
     (dict(scale=-1.0), BAD), (dict(scale=float("nan")), BAD), (dict(scale=float("inf")), BAD),
     (dict(causal=2), BAD), (dict(dtype=2), UNSUP),
+    (dict(B=65536, Hq=65536, Hkv=1, Nq=128, Nk=128), UNSUP),  # 2^32 work-groups: more than one launch holds
 ])
 def test_fwd_rejects(lib, kwargs, status):
     assert fwd(lib, **kwargs) == status
