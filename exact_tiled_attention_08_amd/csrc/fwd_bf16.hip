@@ -485,10 +485,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // over the phase (+1 %, at the cost of P_{j-1} and S_j being live together).
   // The first two groups of a matrix phase (P.V on V_{j-1}, S on K_j) are
   // loaded at the start of the wave's previous softmax phase, so the phase
-  // opens with MFMAs instead of waiting on LDS.  That is safe: both tiles were
-  // copied two steps back and the barrier opening that softmax phase comes
-  // after every wave's wait for those copies; no copy in flight then targets
-  // their buffers.
+  // opens with MFMAs instead of waiting on LDS.  Both tiles were copied two
+  // steps back; the copy waits below make them complete before that softmax
+  // phase in both groups, and no copy in flight then targets their buffers.
   constexpr int PRE = 2;
   bf16x8 fa[4], fb[4];
   auto run_groups = [&]() {
@@ -576,16 +575,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     lr += (lrp[0] + lrp[1]) + (lrp[2] + lrp[3]);
   };
 
-  // Each step issues exactly four copies per wave (K_{j+2}, V_{j+1}).  A
-  // wave's copies of K_{j+1} and V_j (from step j-1) must be complete before
-  // the barrier that ends global phase 2j+1 -- for group 1 that is its first
-  // barrier of step j.  Every wave waits before both of its barriers, leaving
-  // only the four copies of the current step in flight (vmcnt 4); keeping the
-  // loop body free of group-dependent code stops the compiler from cloning it
-  // per group.  lgkmcnt(0) retires this wave's LDS reads before any barrier, so
-  // a buffer is free once the barrier after its last use has passed.
+  // Each step issues exactly four copies per wave (K_{j+2}, V_{j+1}), after
+  // its matrix work.  K_{j+1} and V_j (step j-1's copies) are first read by
+  // the early fragment reads of step j's softmax phase; for group 0 that
+  // phase opens with the barrier in which group 1 ends step j-1.  So every
+  // wave waits for all of its copies (vmcnt 0) before the barrier that ends
+  // its step: a step's copies then have the softmax phase to land, and both
+  // groups' copies of step j-1 are complete before either group reads them.
+  // Before the mid-step barrier a wave only needs the previous step's copies
+  // (vmcnt 4, already true).  The loop body stays free of group-dependent
+  // code, which stops the compiler from cloning it per group.  lgkmcnt(0)
+  // retires this wave's LDS reads before any barrier, so a buffer is free
+  // once the barrier after its last use has passed.
   auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
   auto wait_copies = [&]() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); };
+  auto wait_all_copies = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   // Step 0 multiplies P = 0 by V buffer 2, which no copy has filled yet:
   // give it finite contents.
@@ -594,7 +598,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     copy_tile(kg, 0, kv_lds[0], false);
     copy_tile(kg, 1, kv_lds[1], false);
     copy_tile(vg, 0, kv_lds[3], true);
-    wait_copies();  // K_0 is in
+    wait_all_copies();  // K_0, K_1 and V_0 are in before either group reads them
   }
   barrier();
   if (!lead) barrier();
@@ -619,7 +623,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       set_bufs(b1, b0);  // step j + 1: K_{j+1} in K buffer b1, V_j in V buffer b0
       preload();         // (after the last step: harmless reads that nothing uses)
       softmax_phase(j);
-      wait_copies();
+      wait_all_copies();
       barrier();
     };
     set_bufs(0, 2);
