@@ -36,6 +36,22 @@ def test_prefill_is_deterministic(causal):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("causal", [True, False])
+def test_d64_prefill_is_deterministic(causal):
+    q, k, v, _ = inputs.make_inputs(2, Nq=2048, Nk=2048)
+    q, k, v = q.to(dev()), k.to(dev()), v.to(dev())
+    same_every_time(f"fa_fwd d=64 causal={causal}", lambda: fa.fa_fwd(q, k, v, causal=causal))
+
+
+@pytest.mark.gpu
+def test_packed_prefill_is_deterministic():
+    lens = [1500, 700, 2048, 33]
+    q, k, v, cu_q, cu_k = inputs.make_packed(4, lens, lens, 8, 2, 128)
+    q, k, v, cu_q, cu_k = (t.to(dev()) for t in (q, k, v, cu_q, cu_k))
+    same_every_time("fa_fwd_varlen", lambda: fa.fa_fwd_varlen(q, k, v, cu_q, cu_k, max(lens), causal=True))
+
+
+@pytest.mark.gpu
 def test_padded_gqa_prefill_is_deterministic():
     q, k, v, lens = inputs.make_inputs(4, B=4, Hq=8, Hkv=2, Nq=1500, Nk=1500, len_lo=700, len_hi=1500)
     q, k, v, lens = q.to(dev()), k.to(dev()), v.to(dev()), lens.to(dev())
