@@ -184,6 +184,16 @@ def _decode_shapes(q, k_cache, v_cache):
     return B, Hq, Hkv, Nk, d
 
 
+def _check_decode_out(out, lse, q):
+    """The merge writes B*Hq rows of d outputs and one LSE each: the C ABI
+    cannot see buffer sizes, so they are checked here, before any launch."""
+    B, Hq, _, d = q.shape
+    _check_tensor(out, "out", q.dtype, 4, q.device)
+    _check_tensor(lse, "lse", torch.float32, 3, q.device)
+    if tuple(out.shape) != (B, Hq, 1, d) or tuple(lse.shape) != (B, Hq, 1):
+        raise ValueError(f"out must be [{B}, {Hq}, 1, {d}] and lse [{B}, {Hq}, 1]")
+
+
 def fa_decode_splitkv(q, k_cache, v_cache, num_splits=16, kv_seqlens=None, scale=None,
                       o_part=None, lse_part=None):
     """Split-KV decode partials: (o_part [B,Hq,S,d] f32, lse_part [B,Hq,S] f32)."""
@@ -249,8 +259,7 @@ def fa_decode(q, k_cache, v_cache, kv_seqlens=None, num_splits=16, scale=None, w
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=q.device)
-    _check_tensor(out, "out", q.dtype, 4, q.device)
-    _check_tensor(lse, "lse", torch.float32, 3, q.device)
+    _check_decode_out(out, lse, q)
     s = default_scale(d) if scale is None else float(scale)
     with torch.cuda.device(q.device):  # kernels launch on the current device
         _lib.check(lib.fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, Hq, Hkv, Nk, d,
@@ -288,8 +297,7 @@ def fa_decode_paged(q, k_pages, v_pages, block_table, kv_seqlens, num_splits=16,
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=q.device)
-    _check_tensor(out, "out", q.dtype, 4, q.device)
-    _check_tensor(lse, "lse", torch.float32, 3, q.device)
+    _check_decode_out(out, lse, q)
     s = default_scale(d) if scale is None else float(scale)
     with torch.cuda.device(q.device):  # kernels launch on the current device
         _lib.check(lib.fa_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(out), _ptr(lse),

@@ -206,3 +206,24 @@ def test_large_values_stay_finite():
     q = (q.float() * 8).to(torch.bfloat16)
     k = (k.float() * 8).to(torch.bfloat16)
     check_fwd(q, k, v, causal=True, what="large scores")
+
+
+def test_decode_rejects_wrong_output_shapes():
+    """The merge writes B*Hq rows: a wrong-shaped out or lse is refused in the
+    binding before any kernel is launched (the C ABI cannot see sizes)."""
+    q, k, v = (t.cuda() for t in qkv(2, 4, 2, 1, 100, 128, torch.bfloat16, seed=21))
+    lens = torch.tensor([100, 37], dtype=torch.int32, device="cuda")
+    table = torch.arange(2 * 7, dtype=torch.int32, device="cuda").reshape(2, 7)
+    kp = torch.zeros((14, 2, 16, 128), dtype=torch.bfloat16, device="cuda")
+    good_o = torch.empty((2, 4, 1, 128), dtype=torch.bfloat16, device="cuda")
+    good_l = torch.empty((2, 4, 1), dtype=torch.float32, device="cuda")
+    bad = [(torch.empty((2, 2, 1, 128), dtype=torch.bfloat16, device="cuda"), good_l),
+           (torch.empty((1, 4, 1, 128), dtype=torch.bfloat16, device="cuda"), good_l),
+           (good_o, torch.empty((2, 3, 1), dtype=torch.float32, device="cuda")),
+           (good_o, torch.empty((2, 4, 2), dtype=torch.float32, device="cuda"))]
+    for o, l in bad:
+        with pytest.raises(ValueError):
+            fa.fa_decode(q, k, v, kv_seqlens=lens, out=o, lse=l)
+        with pytest.raises(ValueError):
+            fa.fa_decode_paged(q, kp, kp, table, lens, out=o, lse=l)
+    torch.cuda.synchronize()

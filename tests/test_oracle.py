@@ -105,6 +105,46 @@ def check_two_keys():
         assert abs(L[0, 0, i] - np.logaddexp(s0, s1)) < 1e-13
 
 
+def check_default_scale():
+    """scale=None means the definition's 1/sqrt(d) (concept note, section
+    "是什么"; explainer, section "核心问题").  Keys whose dot products with a
+    query differ by sqrt(d)*ln(3)*a give softmax weights 3^a/(3^a+1) and
+    LSE = ln(3^a + 1) only at that scale; torch's own SDPA default (1/sqrt(E))
+    must agree too.  The oracle rounds the default to fp32 like the kernels,
+    so the closed forms hold to ~1e-7."""
+    for d in (64, 128):
+        q = np.zeros((1, 1, 3, d)); k = np.zeros((1, 1, 2, d))
+        q[0, 0, :, 0] = (1.0, 2.0, -1.0)
+        k[0, 0, 0, 0] = math.sqrt(d) * math.log(3.0)
+        v = rand(1, 1, 2, d)
+        for fn in (lambda: oracle.attention_ref(q, k, v),
+                   lambda: oracle.attention_varlen_ref(q[0], k[0], v[0], [0, 3], [0, 2])):
+            O, L = fn()
+            O, L = O.reshape(3, d), L.reshape(3)
+            for i, a in enumerate((1.0, 2.0, -1.0)):
+                w0 = 3.0 ** a / (3.0 ** a + 1.0)
+                assert np.allclose(O[i], w0 * v[0, 0, 0] + (1 - w0) * v[0, 0, 1], rtol=0, atol=1e-6), (d, a)
+                assert abs(L[i] - math.log(3.0 ** a + 1.0)) < 1e-6, (d, a)
+        # the library's default on random inputs
+        qr, kr, vr = rand(1, 2, 11, d), rand(1, 2, 11, d), rand(1, 2, 11, d)  # Nq = Nk: SDPA aligns causal top-left
+        for causal in (False, True):
+            O, L = oracle.attention_ref(qr, kr, vr, causal=causal)
+            Ot, Lt = _torch_sdpa_default(qr, kr, vr, causal)
+            assert np.allclose(O, Ot, rtol=0, atol=1e-6) and np.allclose(L, Lt, rtol=0, atol=1e-6), (d, causal)
+
+
+def _torch_sdpa_default(q, k, v, causal):
+    """torch CPU fp64 SDPA with no scale argument (its default is 1/sqrt(E)),
+    and the log-sum-exp of the same masked scores."""
+    qt, kt, vt = (torch.from_numpy(x) for x in (q, k, v))
+    O = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=causal).numpy()
+    S = (qt @ kt.transpose(-1, -2)) / math.sqrt(q.shape[-1])
+    if causal:
+        nq, nk = q.shape[2], k.shape[2]
+        S = S.masked_fill(torch.ones(nq, nk, dtype=torch.bool).triu(1), float("-inf"))
+    return O, torch.logsumexp(S, dim=-1).numpy()
+
+
 def check_blocked_recurrence():
     """The concept note's per-block update equals the one-shot softmax."""
     rng = np.random.default_rng(7)
@@ -414,7 +454,7 @@ def check_fp8_attention_dequantised():
 
 
 PIN_CHECKS = [check_rows_sum_to_one, check_constant_v, check_single_key, check_causal_row0,
-              check_zero_q_closed_form, check_two_keys, check_blocked_recurrence,
+              check_zero_q_closed_form, check_two_keys, check_default_scale, check_blocked_recurrence,
               check_key_permutation, check_gqa_equals_mha, check_against_torch_sdpa,
               check_merge_identity, check_split_bounds, check_bwd_finite_differences,
               check_bwd_against_autograd, check_bwd_invariants, check_paged_gather,
@@ -477,6 +517,10 @@ def _mut_lse_drops_max(qh, kh, vh, allowed, scale):
     S = np.where(allowed, scale * (qh @ kh.T), -np.inf)
     m = S.max(axis=1)
     return O, np.where(np.isfinite(m), lse - m, lse), P
+
+
+def _mut_default_scale_over_d(d):
+    return float(np.float32(1.0 / d))
 
 
 def _mut_scale_twice(qh, kh, vh, allowed, scale):
@@ -607,6 +651,7 @@ _ORIG_FP8_ATT = oracle.attention_fp8_ref
 MUTANTS = [("_allowed", _mut_causal_off_by_one), ("_allowed", _mut_padding_inclusive),
            ("_head_map", _mut_head_modulo), ("_one_head", _mut_lse_drops_max),
            ("_one_head", _mut_scale_twice), ("_one_head", _mut_transposed_probs),
+           ("default_scale", _mut_default_scale_over_d),
            ("merge_partials", _mut_merge_unweighted), ("attention_bwd_ref", _mut_bwd_no_rowsum),
            ("attention_bwd_ref", _mut_bwd_unscaled_dq), ("attention_bwd_ref", _mut_bwd_gqa_overwrite),
            ("paged_to_contiguous", _mut_paged_row_reversed),

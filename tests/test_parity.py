@@ -40,7 +40,6 @@ def _sample_rows(n, extra=()):
     return np.array(sorted(r for r in base if 0 <= r < n))
 
 
-@pytest.mark.slow
 def test_cfg3_full_size_sampled_rows():
     q, k, v, _ = inputs.make_inputs(3)
     assert q.shape == (1, 32, 8192, 128)
@@ -48,12 +47,19 @@ def test_cfg3_full_size_sampled_rows():
     check_fwd(q, k, v, causal=True, rows=_sample_rows(8192), heads=heads, what="cfg3 full sampled")
 
 
+@pytest.mark.slow
+def test_cfg3_full_size_every_head_and_row():
+    """Every (head, row) of the long-context workload against the oracle, in the
+    launch configuration the benchmark times."""
+    q, k, v, _ = inputs.make_inputs(3)
+    check_fwd(q, k, v, causal=True, what="cfg3 full, all heads and rows")
+
+
 def test_cfg4_reduced_full_compare():
     q, k, v, lens = inputs.make_inputs(4, Hq=8, Hkv=2, Nq=700, Nk=700, len_lo=300, len_hi=700)
     check_fwd(q, k, v, causal=True, lens=lens, what="cfg4 reduced")
 
 
-@pytest.mark.slow
 def test_cfg4_full_size_sampled_rows():
     q, k, v, lens = inputs.make_inputs(4)
     assert q.shape == (4, 32, 4096, 128) and k.shape == (4, 8, 4096, 128)
@@ -62,6 +68,12 @@ def test_cfg4_full_size_sampled_rows():
     heads = [(b, h) for b in range(4) for h in (0, 5, 30)]
     check_fwd(q, k, v, causal=True, lens=lens, rows=_sample_rows(4096, extra), heads=heads,
               what="cfg4 full sampled")
+
+
+@pytest.mark.slow
+def test_cfg4_full_size_every_head_and_row():
+    q, k, v, lens = inputs.make_inputs(4)
+    check_fwd(q, k, v, causal=True, lens=lens, what="cfg4 full, all heads and rows")
 
 
 def _decode_check(q, k, v, lens, S, sample_pairs=None, what="decode"):
@@ -85,12 +97,28 @@ def test_cfg5_reduced_full_compare():
     _decode_check(q, k, v, None, 16, what="cfg5 reduced")
 
 
-@pytest.mark.slow
 def test_cfg5_full_size_sampled():
     q, k, v, _ = inputs.make_inputs(5)
     assert q.shape == (64, 32, 1, 128) and k.shape == (64, 8, 32768, 128)
     pairs = [(b, hk) for b in (0, 1, 31, 63) for hk in (0, 3, 7)]
     _decode_check(q, k, v, None, 16, sample_pairs=pairs, what="cfg5 full sampled")
+
+
+@pytest.mark.slow
+def test_cfg5_full_size_every_sequence_and_head():
+    """All 64 sequences x 32 query heads of the decode workload; the oracle runs
+    one sequence at a time so the host never holds the whole cache in fp64."""
+    q, k, v, _ = inputs.make_inputs(5)
+    qd, kd, vd = to_dev(q, k, v)
+    log(f"  fa_decode q{tuple(q.shape)} cache{tuple(k.shape)} S=16")
+    o, lse = fa.fa_decode(qd, kd, vd, num_splits=16)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    del qd, kd, vd
+    O_ref = np.empty(tuple(o.shape)); L_ref = np.empty(tuple(lse.shape))
+    for b in range(q.shape[0]):
+        O_ref[b:b + 1], L_ref[b:b + 1] = oracle.attention_ref(q[b:b + 1], k[b:b + 1], v[b:b + 1])
+    compare(o, lse, O_ref, L_ref, q.dtype, "cfg5 full, all sequences and heads")
 
 
 def test_cfg5_partials_match_oracle_partials():
