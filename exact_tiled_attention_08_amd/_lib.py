@@ -30,6 +30,9 @@ PROTOTYPES = {
     "fa_status_string": (ctypes.c_char_p, [_i]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_version": (_i, []),
+    # measurement aids (include/fa_ceilings.h)
+    "fa_ceiling_mfma": (_i, [_p, _i, _i, _p]),
+    "fa_ceiling_read": (_i, [_p, _sz, _p, _i, _p]),
 }
 
 _lib = None

@@ -90,6 +90,24 @@ fa::AttnArgs make_args(const void* q, const void* k, const void* v, void* o, flo
   return a;
 }
 
+// Both decode stages on a workspace the caller validated (or the static
+// scratch): partials, then the merge.
+int decode_launch(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int Hq,
+                  int Hkv, int Nk, int d, float scale, const int32_t* kv_seqlens, int num_splits, void* workspace,
+                  int dtype, void* stream) {
+  const size_t rows = (size_t)B * Hq;
+  float* o_part = (float*)workspace;
+  float* lse_part = (float*)((char*)workspace + lse_offset(rows * num_splits * d * sizeof(float)));
+  fa::AttnArgs a = make_args(q, k_cache, v_cache, nullptr, nullptr, kv_seqlens, B, Hq, Hkv, 1, Nk, d, scale, 0,
+                             stream);
+  fa::PartialOut part{o_part, lse_part, num_splits};
+  hipError_t e = dtype == FA_BF16 ? fa::launch_decode_splitkv_bf16(a, part) : fa::launch_fwd_f32(a, &part);
+  if (e != hipSuccess) return hip_status(e, "fa_decode split stage launch");
+  return hip_status(fa::launch_lse_merge(o_part, lse_part, o, lse, (int)rows, d, num_splits, dtype == FA_BF16,
+                                         (hipStream_t)stream),
+                    "fa_decode merge stage launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -241,18 +259,10 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, 
   if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
   if (kv_seqlens != nullptr && !aligned(kv_seqlens, 4))
     return fail(FA_ERR_INVALID_ARG, "kv_seqlens is not 4-byte aligned");
-  const size_t rows = (size_t)B * Hq;
-  float* o_part = (float*)workspace;
-  float* lse_part = (float*)((char*)workspace + lse_offset(rows * num_splits * d * sizeof(float)));
-  fa::AttnArgs a = make_args(q, k_cache, v_cache, nullptr, nullptr, kv_seqlens, B, Hq, Hkv, 1, Nk, d, scale, 0,
-                             stream);
-  fa::PartialOut part{o_part, lse_part, num_splits};
-  hipError_t e = dtype == FA_BF16 ? fa::launch_decode_splitkv_bf16(a, part) : fa::launch_fwd_f32(a, &part);
-  if (e != hipSuccess) return hip_status(e, "fa_decode split stage launch");
-  return hip_status(fa::launch_lse_merge(o_part, lse_part, o, lse, (int)rows, d, num_splits, dtype == FA_BF16,
-                                         (hipStream_t)stream),
-                    "fa_decode merge stage launch");
+  return decode_launch(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nk, d, scale, kv_seqlens, num_splits, workspace,
+                       dtype, stream);
 }
+
 
 
 int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table, void* o,

@@ -1,0 +1,82 @@
+// Measured ceilings for the roofline denominators: what this GPU actually
+// sustains for the two resources the attention kernels are bound by.
+//
+//  * ceiling_mfma_kernel: nothing but v_mfma_f32_32x32x16_bf16 on register
+//    operands, four independent accumulator chains per wave, two waves per
+//    SIMD -- the matrix-core rate the prefill can at best approach.
+//  * ceiling_read_kernel: a streaming read of a large buffer with 16-byte
+//    nontemporal loads, four in flight per lane -- the HBM rate the decode can
+//    at best approach.
+//
+// These are measurement aids; no attention entry point uses them.
+#include "fa_ceilings.h"
+
+#include <hip/hip_runtime.h>
+
+#include "fa_device.hpp"
+
+namespace fa {
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ceiling_mfma_kernel(float* out,
+                                                                                                   int iters) {
+  const int tid = threadIdx.x;
+  // Operands depend on the thread so nothing folds; values stay tiny so the
+  // accumulators never overflow.
+  bf16x8 a, b;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    a[t] = (__bf16)((float)((tid + t) & 7) * 0.0078125f);
+    b[t] = (__bf16)((float)((tid * 3 + t) & 7) * 0.0078125f);
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = f32x16{};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = mfma32x32x16(a, b, acc[c]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  out[(size_t)blockIdx.x * 256 + tid] = s;
+}
+
+__global__ __launch_bounds__(256) void ceiling_read_kernel(const u32x4* __restrict__ src, size_t n16,
+                                                           unsigned* out) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  unsigned acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    u32x4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= x[u][0] ^ x[u][1] ^ x[u][2] ^ x[u][3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 x = __builtin_nontemporal_load(src + i);
+    acc ^= x[0] ^ x[1] ^ x[2] ^ x[3];
+  }
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+}  // namespace fa
+
+extern "C" {
+
+int fa_ceiling_mfma(float* out, int blocks, int iters, void* stream) {
+  if (out == nullptr || blocks < 1 || iters < 1) return -1;
+  hipLaunchKernelGGL(fa::ceiling_mfma_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int fa_ceiling_read(const void* src, size_t bytes, unsigned* out, int blocks, void* stream) {
+  if (src == nullptr || out == nullptr || blocks < 1 || bytes % 16 != 0 || ((uintptr_t)src % 16) != 0) return -1;
+  hipLaunchKernelGGL(fa::ceiling_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                     (const fa::u32x4*)src, bytes / 16, out);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // extern "C"

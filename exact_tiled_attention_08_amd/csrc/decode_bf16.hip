@@ -292,48 +292,83 @@ hipError_t launch_decode_splitkv_bf16(const AttnArgs& a, const PartialOut& part,
 // ---------------------------------------------------------------------------
 // Exact merge: per row, M = max_s lse_s, w_s = e^(lse_s - M),
 // O = sum_s w_s O_s / sum_s w_s, LSE = M + ln sum_s w_s.
+// One wave per row, four rows per work-group: the wave reads the row's S LSEs
+// once (lane s, s + 64, ...), reduces M and sum_s w_s across lanes, keeps the
+// weights in LDS, and then streams the S partial rows with every lane owning
+// D / 64 adjacent outputs (one 8-byte load per split for D = 128).
 template <int D, bool BF16>
-__global__ __launch_bounds__(D) void lse_merge_kernel(const float* __restrict__ o_part,
-                                                      const float* __restrict__ lse_part, void* o,
-                                                      float* lse, int S) {
-  const size_t row = blockIdx.x;
-  const int dd = threadIdx.x;
+__global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict__ o_part,
+                                                       const float* __restrict__ lse_part, void* o, float* lse,
+                                                       int S, int rows) {
+  constexpr int E = D / 64;  // outputs per lane
+  __shared__ float wsh[4][FA_MAX_SPLITS];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row_i = blockIdx.x * 4 + wave;
+  const bool live = row_i < rows;
+  const size_t row = live ? (size_t)row_i : 0;
   const float* lp = lse_part + row * S;
   float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lp[s]);
+  if (live)
+    for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[s]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
   const float M_use = (M == kNegInf) ? 0.f : M;
-  float acc = 0.f, tot = 0.f;
-  const float* op = o_part + row * S * D + dd;
+  float tot = 0.f;
+  if (live)
+    for (int s = lane; s < S; s += 64) {
+      const float w = fast_exp2((lp[s] - M_use) * kLog2e);
+      wsh[wave][s] = w;
+      tot += w;
+    }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
+  __syncthreads();
+  if (!live) return;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  const float* op = o_part + row * S * D + lane * E;
+#pragma unroll 4
   for (int s = 0; s < S; ++s) {
-    const float w = __expf(lp[s] - M_use);
-    tot += w;
-    acc += w * op[(size_t)s * D];
+    const float w = wsh[wave][s];
+    if constexpr (E == 2) {
+      const float2 x = *(const float2*)(op + (size_t)s * D);
+      acc[0] += w * x.x;
+      acc[1] += w * x.y;
+    } else {
+      acc[0] += w * op[(size_t)s * D];
+    }
   }
-  const float out = tot > 0.f ? acc / tot : 0.f;
-  if (BF16) {
-    ((__bf16*)o)[row * D + dd] = (__bf16)out;
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  if constexpr (BF16) {
+    __bf16* ob = (__bf16*)o + row * D + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) ob[e] = (__bf16)(acc[e] * inv);
   } else {
-    ((float*)o)[row * D + dd] = out;
+    float* of = (float*)o + row * D + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) of[e] = acc[e] * inv;
   }
-  if (dd == 0) lse[row] = tot > 0.f ? M_use + __logf(tot) : kNegInf;
+  if (lane == 0) lse[row] = tot > 0.f ? M_use + __log2f(tot) * kLn2 : kNegInf;
 }
 
 hipError_t launch_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse, int rows,
                             int d, int num_splits, bool out_bf16, hipStream_t stream) {
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
   if (d == 128) {
     if (out_bf16)
-      hipLaunchKernelGGL((lse_merge_kernel<128, true>), dim3(rows), dim3(128), 0, stream, o_part, lse_part, o,
-                         lse, num_splits);
+      hipLaunchKernelGGL((lse_merge_kernel<128, true>), grid, block, 0, stream, o_part, lse_part, o, lse,
+                         num_splits, rows);
     else
-      hipLaunchKernelGGL((lse_merge_kernel<128, false>), dim3(rows), dim3(128), 0, stream, o_part, lse_part, o,
-                         lse, num_splits);
+      hipLaunchKernelGGL((lse_merge_kernel<128, false>), grid, block, 0, stream, o_part, lse_part, o, lse,
+                         num_splits, rows);
   } else {
     if (out_bf16)
-      hipLaunchKernelGGL((lse_merge_kernel<64, true>), dim3(rows), dim3(64), 0, stream, o_part, lse_part, o,
-                         lse, num_splits);
+      hipLaunchKernelGGL((lse_merge_kernel<64, true>), grid, block, 0, stream, o_part, lse_part, o, lse,
+                         num_splits, rows);
     else
-      hipLaunchKernelGGL((lse_merge_kernel<64, false>), dim3(rows), dim3(64), 0, stream, o_part, lse_part, o,
-                         lse, num_splits);
+      hipLaunchKernelGGL((lse_merge_kernel<64, false>), grid, block, 0, stream, o_part, lse_part, o, lse,
+                         num_splits, rows);
   }
   return hipGetLastError();
 }

@@ -326,8 +326,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 //   phase 2j+1 : group 0 softmax(j)     group 1 matrix(j)
 //
 // Both groups run the same program -- matrix(j), barrier, softmax(j),
-// barrier -- group 1 simply starting one barrier later.  K/V tiles rotate
-// through three LDS buffers; step j starts copying K_{j+2} and V_{j+1}.
+// barrier -- group 1 simply starting one barrier later.  K and V tiles rotate
+// through rings of NBUF LDS buffers each; step j starts copying K_{j+NBUF-1}
+// and V_{j+NBUF-2} (the furthest a ring of NBUF buffers allows: one tile more
+// and a copy would overwrite a tile the lagging group still reads).  With
+// NBUF = 4 every copy has three phases to land before it is waited on.
+//
+// Under a causal mask query tile i sees i+1 times the keys of tile 0; with
+// PAIR a work-group runs tile i and then tile n-1-i, so every work-group of a
+// head does the same work and the grid has no long tail.
 struct PPTile {
   static constexpr int D = 128, BM = 256, BN = 64, WAVES = 8, THREADS = 512;
   static constexpr int TILE = BN * D;                 // elements per K or V tile (16 KiB)
@@ -335,12 +342,14 @@ struct PPTile {
   static constexpr int COPIES = BN / RPI / WAVES;     // 1 KiB copies per wave per tile (= 2)
 };
 
-template <bool CAUSAL, int MODE>
+template <bool CAUSAL, int MODE, int NBUF, bool PAIR>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_pp_kernel(FwdParams p) {
   using T = PPTile;
   constexpr int D = T::D, BM = T::BM, BN = T::BN;
-  // buffers 0..2: K tiles, 3..5: V tiles; tile t lives in buffer t % 3.
-  __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[6][T::TILE];
+  static_assert(NBUF == 3 || NBUF == 4, "ring depth");
+  constexpr int KAHEAD = NBUF - 1, VAHEAD = NBUF - 2;  // tiles copied ahead of the one being used
+  // buffers 0..NBUF-1: K tiles, NBUF..2*NBUF-1: V tiles; tile t lives in buffer t % NBUF.
+  __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[2 * NBUF][T::TILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -350,310 +359,339 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int bh_count = p.B * p.Hq;
   const int bh = blockIdx.x % bh_count;
-  const int qt = p.n_qtiles - 1 - (int)(blockIdx.x / bh_count);
+  const int slot = (int)(blockIdx.x / bh_count);
   const int b = bh / p.Hq, hq = bh - b * p.Hq;
   const int hk = hq / (p.Hq / p.Hkv);
 
   const SeqRows sr = seq_rows<MODE>(p, b, hq, hk);
   const int nq = sr.nq, kv_len = sr.kv_len;
-  const int q0 = qt * BM;
-  if (MODE == kPacked && q0 >= nq) return;  // a sequence shorter than the longest one
   const int diag = sr.nk - nq;
-  int kend = kv_len;
-  if (CAUSAL) kend = min(kend, min(q0 + BM, nq) - 1 + diag + 1);
-  const int n_kt = kend > 0 ? (kend + BN - 1) / BN : 0;
-  // tiles this wave's rows can see at all (later tiles are skipped, not masked)
-  const int w_first = q0 + wave_u * 32;
-  int w_kend = kv_len;
-  if (CAUSAL) w_kend = min(w_kend, min(w_first + 32, nq) - 1 + diag + 1);
-  const int w_nkt = w_kend > 0 ? (w_kend + BN - 1) / BN : 0;
-
   const size_t q_base = sr.q_row0;
   const uint16_t* kg = p.k + sr.kv_row0 * D;
   const uint16_t* vg = p.v + sr.kv_row0 * D;
 
-  const int qrow = w_first + li;
-  bf16x8 qf[D / 16];
-  if (qrow < nq) {
-    const uint16_t* qp = p.q + (q_base + qrow) * D + 8 * hi;
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) qf[st] = *(const bf16x8*)(qp + 16 * st);
-  } else {
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) qf[st] = bf16x8{};
-  }
+  // Work-group -> query tiles.  Without PAIR: one tile, the heaviest causal
+  // tiles dispatched first.  With PAIR: tiles slot and n-1-slot (one tile
+  // when they coincide).
+  const int n_tiles_here = PAIR ? ((p.n_qtiles - 1 - slot) > slot ? 2 : 1) : 1;
+  for (int ti = 0; ti < n_tiles_here; ++ti) {
+    const int qt = PAIR ? (ti == 0 ? slot : p.n_qtiles - 1 - slot) : p.n_qtiles - 1 - slot;
+    const int q0 = qt * BM;
+    if (MODE == kPacked && q0 >= nq) continue;  // a sequence shorter than the longest one (uniform)
+    int kend = kv_len;
+    if (CAUSAL) kend = min(kend, min(q0 + BM, nq) - 1 + diag + 1);
+    const int n_kt = kend > 0 ? (kend + BN - 1) / BN : 0;
+    // tiles this wave's rows can see at all (later tiles are skipped, not masked)
+    const int w_first = q0 + wave_u * 32;
+    int w_kend = kv_len;
+    if (CAUSAL) w_kend = min(w_kend, min(w_first + 32, nq) - 1 + diag + 1);
+    const int w_nkt = w_kend > 0 ? (w_kend + BN - 1) / BN : 0;
 
-  // Retire the Q loads here.  Their first use is inside the tile loop, and
-  // the compiler's wait for them there would be a vmcnt count that, in every
-  // later step, also waits for that step's K/V copies.
+    const int qrow = w_first + li;
+    bf16x8 qf[D / 16];
+    if (qrow < nq) {
+      const uint16_t* qp = p.q + (q_base + qrow) * D + 8 * hi;
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st) asm volatile("" : "+v"(qf[st]));
-
-  float m = kNegInf, l = 0.f, lr = 0.f;
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-  f32x16 s[BN / 32];   // S_j, from its matrix phase to its softmax phase
-  bf16x8 pf[BN / 16];  // P_j, from its softmax phase to the next matrix phase
-#pragma unroll
-  for (int kb = 0; kb < BN / 32; ++kb) s[kb] = f32x16{};
-#pragma unroll
-  for (int i = 0; i < BN / 16; ++i) pf[i] = bf16x8{};
-
-  // Copy plan: wave w moves the 1 KiB copies c = 2w, 2w+1 (rows 4c .. 4c+3) of
-  // each K and V tile; lane l brings row 4c + l/16, source chunk
-  // (l % 16) ^ swizzle(row), to LDS position l % 16 (K: swz, V: swz_v128).
-  // Tiles past the last one are clamped to it: the copy then lands in a
-  // buffer no phase reads, which keeps exactly four copies per step.
-  // The lane offsets of a full tile's copies are the same for every tile:
-  // computed once here (bytes; the first copy's carries the +1 KiB bias of
-  // copy16x2_to_lds).  Only the last tile of a sequence, where rows past the
-  // length re-read the last valid row, adjusts them.
-  static_assert(T::COPIES == 2, "copies are issued in pairs");
-  const int cp_r0 = (wave_u * T::COPIES) * T::RPI + (lane >> 4), cp_r1 = cp_r0 + T::RPI;
-  int cp_k0 = (cp_r0 * D + (((lane & 15) ^ swz<D>(cp_r0)) * 8)) * 2 + 1024;
-  int cp_k1 = (cp_r1 * D + (((lane & 15) ^ swz<D>(cp_r1)) * 8)) * 2;
-  int cp_v0 = (cp_r0 * D + (((lane & 15) ^ swz_v128(cp_r0)) * 8)) * 2 + 1024;
-  int cp_v1 = (cp_r1 * D + (((lane & 15) ^ swz_v128(cp_r1)) * 8)) * 2;
-  asm volatile("" : "+v"(cp_k0), "+v"(cp_k1), "+v"(cp_v0), "+v"(cp_v1));
-  auto copy_tile = [&](const uint16_t* src, int t, uint16_t* dst, bool is_v) {
-    t = min(t, n_kt - 1);
-    const int k0 = t * BN;
-    const uint16_t* base = src + (size_t)k0 * D;
-    int o0 = is_v ? cp_v0 : cp_k0, o1 = is_v ? cp_v1 : cp_k1;
-    if (k0 + BN > kv_len) {  // rows past the length re-read the last valid row
-      o0 -= max(0, k0 + cp_r0 - (kv_len - 1)) * (2 * D);
-      o1 -= max(0, k0 + cp_r1 - (kv_len - 1)) * (2 * D);
-    }
-    // the wave's two copies are adjacent in LDS: one m0 setting serves both
-    copy16x2_to_lds((const char*)base - 1024, o0, o1, dst + wave_u * T::COPIES * 512);
-  };
-
-  int k_off[D / 16];
-#pragma unroll
-  for (int st = 0; st < D / 16; ++st) k_off[st] = li * D + (((2 * st + hi) ^ swz<D>(li)) * 8);
-  const int tr_r = 4 * hi + ((lane & 15) >> 2);
-  const int tr_cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int tr_in = 4 * (lane & 1);
-  int v_off[D / 32];  // row tr_r; the second read of a pair is 8 rows on
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)  // V region starts at buffer 3
-    v_off[db] = 3 * T::TILE + tr_r * D + (((4 * db + tr_cc) ^ swz_v128(tr_r)) * 8) + tr_in;
-  // Fragment reads address lds0 + (per-step address register) + (a
-  // compile-time offset): the step adds its buffer's base to the lane offsets
-  // once, so one loop body serves every buffer.  The empty asm hides the lane
-  // offsets' known bits, so the compiler keeps the constant parts as additions
-  // it can fold into the DS instructions' offset field (the library is built
-  // with DS offset folding allowed: these addresses are never negative).
-#pragma unroll
-  for (int st = 0; st < D / 16; ++st) asm volatile("" : "+v"(k_off[st]));
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) asm volatile("" : "+v"(v_off[db]));
-  const uint16_t* lds0 = kv_lds[0];
-  int ka[D / 16], va[D / 32];  // this step's K / V fragment offsets (elements)
-  // Consecutive MFMAs always accumulate into different registers: a chain of
-  // dependent MFMAs on one accumulator issues far below the matrix-core rate,
-  // two or more interleaved chains keep it busy.
-  //   S group g (0..3): k-steps 2g, 2g+1 for both key blocks, alternating
-  //   P.V group 4+i:    key slice i (16 keys) for all four d-blocks
-  auto load_group = [&](int g, bf16x8* f) {
-    if (g < 4) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) f[i] = *(const bf16x8*)(lds0 + ka[2 * g + (i >> 1)] + (i & 1) * 32 * D);
+      for (int st = 0; st < D / 16; ++st) qf[st] = *(const bf16x8*)(qp + 16 * st);
     } else {
-      const int c = (((g - 4) >> 1) * 32 + 16 * ((g - 4) & 1)) * D;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        f[db] = join_bf16x8(lds_read_tr16(lds0 + va[db] + c), lds_read_tr16(lds0 + va[db] + c + 8 * D));
+      for (int st = 0; st < D / 16; ++st) qf[st] = bf16x8{};
     }
-  };
-  auto mfma_group = [&](int g, const bf16x8* f) {
-    if (g < 4) {
+    // Retire the Q loads here.  Their first use is inside the tile loop, and
+    // the compiler's wait for them there would be a vmcnt count that, in every
+    // later step, also waits for that step's K/V copies.
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kb = i & 1, st = 2 * g + (i >> 1);
-        s[kb] = mfma32x32x16(f[i], qf[st], st == 0 ? f32x16{} : s[kb]);
+    for (int st = 0; st < D / 16; ++st) asm volatile("" : "+v"(qf[st]));
+
+    // Per-lane LDS offsets of the fragment reads (elements), the same for
+    // every tile.  K: row li of a 32-key block, chunk 2*st + hi; V (transposed
+    // 4x16 reads): row tr_r (the second read of a pair is 8 rows on).
+    int k_off[D / 16];
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) k_off[st] = li * D + (((2 * st + hi) ^ swz<D>(li)) * 8);
+    const int tr_r = 4 * hi + ((lane & 15) >> 2);
+    const int tr_cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int tr_in = 4 * (lane & 1);
+    int v_off[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)  // V region starts at buffer NBUF
+      v_off[db] = NBUF * T::TILE + tr_r * D + (((4 * db + tr_cc) ^ swz_v128(tr_r)) * 8) + tr_in;
+    // Fragment reads address lds0 + (per-step address register) + (a
+    // compile-time offset): the step adds its buffer's base to the lane offsets
+    // once, so one loop body serves every buffer.  The empty asm hides the lane
+    // offsets' known bits, so the compiler keeps the constant parts as additions
+    // it can fold into the DS instructions' offset field (the library is built
+    // with DS offset folding allowed: these addresses are never negative).
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) asm volatile("" : "+v"(k_off[st]));
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) asm volatile("" : "+v"(v_off[db]));
+    const uint16_t* lds0 = kv_lds[0];
+
+    // Copy plan: wave w moves the 1 KiB copies c = 2w, 2w+1 (rows 4c .. 4c+3) of
+    // each K and V tile; lane l brings row 4c + l/16, source chunk
+    // (l % 16) ^ swizzle(row), to LDS position l % 16 (K: swz, V: swz_v128).
+    // The lane offsets of a full tile's copies are the same for every tile:
+    // computed once here (bytes; the first copy's carries the +1 KiB bias of
+    // copy16x2_to_lds).  Only the last tile of a sequence, where rows past the
+    // length re-read the last valid row, adjusts them.
+    static_assert(T::COPIES == 2, "copies are issued in pairs");
+    const int cp_r0 = (wave_u * T::COPIES) * T::RPI + (lane >> 4), cp_r1 = cp_r0 + T::RPI;
+    int cp_k0 = (cp_r0 * D + (((lane & 15) ^ swz<D>(cp_r0)) * 8)) * 2 + 1024;
+    int cp_k1 = (cp_r1 * D + (((lane & 15) ^ swz<D>(cp_r1)) * 8)) * 2;
+    int cp_v0 = (cp_r0 * D + (((lane & 15) ^ swz_v128(cp_r0)) * 8)) * 2 + 1024;
+    int cp_v1 = (cp_r1 * D + (((lane & 15) ^ swz_v128(cp_r1)) * 8)) * 2;
+    asm volatile("" : "+v"(cp_k0), "+v"(cp_k1), "+v"(cp_v0), "+v"(cp_v1));
+
+    float m = kNegInf, l = 0.f, lr = 0.f;
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+    f32x16 s[BN / 32];   // S_j, from its matrix phase to its softmax phase
+    bf16x8 pf[BN / 16];  // P_j, from its softmax phase to the next matrix phase
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < BN / 16; ++i) pf[i] = bf16x8{};
+
+    // Tiles past the last one are clamped to it: the copy then lands in a
+    // buffer no phase reads, which keeps exactly four copies per step.
+    auto copy_tile = [&](const uint16_t* src, int t, uint16_t* dst, bool is_v) {
+      t = min(t, n_kt - 1);
+      const int k0 = t * BN;
+      const uint16_t* base = src + (size_t)k0 * D;
+      int o0 = is_v ? cp_v0 : cp_k0, o1 = is_v ? cp_v1 : cp_k1;
+      if (k0 + BN > kv_len) {  // rows past the length re-read the last valid row
+        o0 -= max(0, k0 + cp_r0 - (kv_len - 1)) * (2 * D);
+        o1 -= max(0, k0 + cp_r1 - (kv_len - 1)) * (2 * D);
       }
-    } else {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32x32x16(f[db], pf[g - 4], oacc[db]);
-    }
-  };
-  // The pipeline alternates P.V groups (G4..G7) and S groups (G0..G3): the
-  // P.V groups' transposed V reads move half the bytes per LDS cycle of the
-  // S groups' K reads, and alternating the two spreads the LDS demand evenly
-  // over the phase (+1 %, at the cost of P_{j-1} and S_j being live together).
-  // The first two groups of a matrix phase (P.V on V_{j-1}, S on K_j) are
-  // loaded at the start of the wave's previous softmax phase, so the phase
-  // opens with MFMAs instead of waiting on LDS.  Both tiles were copied two
-  // steps back; the copy waits below make them complete before that softmax
-  // phase in both groups, and no copy in flight then targets their buffers.
-  constexpr int PRE = 2;
-  bf16x8 fa[4], fb[4];
-  auto run_groups = [&]() {
-    auto grp = [](int i) { return (i & 1) ? (i >> 1) : 4 + (i >> 1); };
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i + 1 < 8 && i + 1 >= PRE) load_group(grp(i + 1), (i & 1) ? fa : fb);
-      mfma_group(grp(i), (i & 1) ? fb : fa);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  auto preload = [&]() {
-    load_group(4, fa);
-    load_group(0, fb);
-  };
-  // Every step runs all eight groups -- one code path keeps the register
-  // allocation tight.  Work a wave does not need is harmless: S_j of a tile
-  // past the wave's range is never used, and P.V runs with P = 0 (at j = 0,
-  // and after a skipped softmax) against finite V data.
-  auto set_bufs = [&](int kbuf, int vbuf) {
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) ka[st] = k_off[st] + kbuf * T::TILE;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) va[db] = v_off[db] + vbuf * T::TILE;
-  };
+      // the wave's two copies are adjacent in LDS: one m0 setting serves both
+      copy16x2_to_lds((const char*)base - 1024, o0, o1, dst + wave_u * T::COPIES * 512);
+    };
 
-  // Online-softmax update for tile j (S_j -> P_j), as in the 4-wave kernel.
-  auto softmax_phase = [&](int j) {
-    if (j >= w_nkt) {
+    int ka[D / 16], va[D / 32];  // this step's K / V fragment offsets (elements)
+    // Consecutive MFMAs always accumulate into different registers: a chain of
+    // dependent MFMAs on one accumulator issues far below the matrix-core rate,
+    // two or more interleaved chains keep it busy.
+    //   S group g (0..3): k-steps 2g, 2g+1 for both key blocks, alternating
+    //   P.V group 4+i:    key slice i (16 keys) for all four d-blocks
+    auto load_group = [&](int g, bf16x8* f) {
+      if (g < 4) {
 #pragma unroll
-      for (int i = 0; i < BN / 16; ++i) pf[i] = bf16x8{};
-      return;
-    }
-    const int k0 = j * BN;
-    const bool need_mask = (k0 + BN > kv_len) || (CAUSAL && k0 + BN - 1 > w_first + diag);
-    if (need_mask) {
-      // key k0 + 4*hi + c(kb, r) is visible iff c < rel
-      const int rel = (CAUSAL ? min(kv_len, qrow + diag + 1) : kv_len) - k0 - 4 * hi;
+        for (int i = 0; i < 4; ++i) f[i] = *(const bf16x8*)(lds0 + ka[2 * g + (i >> 1)] + (i & 1) * 32 * D);
+      } else {
+        const int c = (((g - 4) >> 1) * 32 + 16 * ((g - 4) & 1)) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          f[db] = join_bf16x8(lds_read_tr16(lds0 + va[db] + c), lds_read_tr16(lds0 + va[db] + c + 8 * D));
+      }
+    };
+    auto mfma_group = [&](int g, const bf16x8* f) {
+      if (g < 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kb = i & 1, st = 2 * g + (i >> 1);
+          s[kb] = mfma32x32x16(f[i], qf[st], st == 0 ? f32x16{} : s[kb]);
+        }
+      } else {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32x32x16(f[db], pf[g - 4], oacc[db]);
+      }
+    };
+    // The pipeline alternates P.V groups (G4..G7) and S groups (G0..G3): the
+    // P.V groups' transposed V reads move half the bytes per LDS cycle of the
+    // S groups' K reads, and alternating the two spreads the LDS demand evenly
+    // over the phase.  The first two groups of a matrix phase (P.V on V_{j-1},
+    // S on K_j) are loaded at the start of the wave's previous softmax phase,
+    // so the phase opens with MFMAs instead of waiting on LDS.  Both tiles were
+    // copied at least two steps back; the copy waits below make them complete
+    // before that softmax phase in both groups, and no copy in flight then
+    // targets their buffers.
+    constexpr int PRE = 2;
+    bf16x8 fa[4], fb[4];
+    auto run_groups = [&]() {
+      auto grp = [](int i) { return (i & 1) ? (i >> 1) : 4 + (i >> 1); };
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i + 1 < 8 && i + 1 >= PRE) load_group(grp(i + 1), (i & 1) ? fa : fb);
+        mfma_group(grp(i), (i & 1) ? fb : fa);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto preload = [&]() {
+      load_group(4, fa);
+      load_group(0, fb);
+    };
+    // Every step runs all eight groups -- one code path keeps the register
+    // allocation tight.  Work a wave does not need is harmless: S_j of a tile
+    // past the wave's range is never used, and P.V runs with P = 0 (at j = 0,
+    // and after a skipped softmax) against finite V data.
+    auto set_bufs = [&](int kbuf, int vbuf) {
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) ka[st] = k_off[st] + kbuf * T::TILE;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) va[db] = v_off[db] + vbuf * T::TILE;
+    };
+
+    // Online-softmax update for tile j (S_j -> P_j), as in the 4-wave kernel.
+    auto softmax_phase = [&](int j) {
+      if (j >= w_nkt) {
+#pragma unroll
+        for (int i = 0; i < BN / 16; ++i) pf[i] = bf16x8{};
+        return;
+      }
+      const int k0 = j * BN;
+      const bool need_mask = (k0 + BN > kv_len) || (CAUSAL && k0 + BN - 1 > w_first + diag);
+      if (need_mask) {
+        // key k0 + 4*hi + c(kb, r) is visible iff c < rel
+        const int rel = (CAUSAL ? min(kv_len, qrow + diag + 1) : kv_len) - k0 - 4 * hi;
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= rel) s[kb][r] = kNegInf;
+      }
+      // Row max, exponentials and the two row sums, with the reductions split
+      // into four independent partial chains (short dependency chains keep the
+      // vector ALU busy).
+      float mxp[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 8 * (r >> 2) + (r & 3) >= rel) s[kb][r] = kNegInf;
+        for (int r = 0; r < 16; ++r) mxp[r & 3] = fmaxf(mxp[r & 3], s[kb][r]);
+      float mx = fmaxf(fmaxf(mxp[0], mxp[1]), fmaxf(mxp[2], mxp[3]));
+      mx = pair_max32(mx) * p.scale_log2;
+      if (__any(mx > m + kRescaleSlack)) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - ((m_new == kNegInf) ? 0.f : m_new));
+        m = m_new;
+        l *= alpha;
+        lr *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      const float m_use = (m == kNegInf) ? 0.f : m;
+      float rsp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], p.scale_log2, -m_use));
+          rsp[r & 3] += s[kb][r];
+        }
+      l += (rsp[0] + rsp[1]) + (rsp[2] + rsp[3]);
+      float lrp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          float t[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) t[e] = s[kb][8 * mm + e];
+          pf[kb * 2 + mm] = pack_bf16x8_sum(t, lrp[kb * 2 + mm]);
+        }
+      lr += (lrp[0] + lrp[1]) + (lrp[2] + lrp[3]);
+    };
+
+    // Each step issues exactly four copy instructions per wave (K_{j+KAHEAD},
+    // V_{j+VAHEAD}), after its matrix work.  Step j's softmax phase reads the
+    // early fragments of K_{j+1} and V_j, copied NBUF-2 steps before; for
+    // group 0 that phase opens with the barrier in which group 1 ends step
+    // j-1.  So every wave waits, before the barrier that ends its step, for
+    // all copies older than its last NBUF-3 steps' (vmcnt 0 with three
+    // buffers, vmcnt 4 with four): those copies are then complete in both
+    // groups before either group reads them.  Before the mid-step barrier the
+    // wait allows NBUF-2 steps of copies in flight and is already met.  The
+    // loop body stays free of group-dependent code, which stops the compiler
+    // from cloning it per group.  lgkmcnt(0) retires this wave's LDS reads
+    // before any barrier, so a buffer is free once the barrier after its last
+    // use has passed.  (tests/test_schedule_model.py replays this schedule.)
+    auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+    auto wait_mid = [&]() {
+      if constexpr (NBUF == 3) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    };
+    auto wait_end = [&]() {
+      if constexpr (NBUF == 3) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    };
+    auto wait_all_copies = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+    // Step 0 multiplies P = 0 by V buffer NBUF-1 (V_{-1}), which no copy has
+    // filled yet: give it finite contents.
+    for (int i = tid; i < T::TILE / 8; i += T::THREADS) ((uint4*)kv_lds[2 * NBUF - 1])[i] = uint4{0, 0, 0, 0};
+    if (n_kt > 0) {
+#pragma unroll
+      for (int t = 0; t < KAHEAD; ++t) copy_tile(kg, t, kv_lds[t], false);
+#pragma unroll
+      for (int t = 0; t < VAHEAD; ++t) copy_tile(vg, t, kv_lds[NBUF + t], true);
+      wait_all_copies();  // the first tiles are in before either group reads them
     }
-    // Row max, exponentials and the two row sums, with the reductions split
-    // into four independent partial chains (short dependency chains keep the
-    // vector ALU busy).
-    float mxp[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mxp[r & 3] = fmaxf(mxp[r & 3], s[kb][r]);
-    float mx = fmaxf(fmaxf(mxp[0], mxp[1]), fmaxf(mxp[2], mxp[3]));
-    mx = pair_max32(mx) * p.scale_log2;
-    if (__any(mx > m + kRescaleSlack)) {
-      const float m_new = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - ((m_new == kNegInf) ? 0.f : m_new));
-      m = m_new;
-      l *= alpha;
-      lr *= alpha;
+    barrier();
+    if (!lead) barrier();
+    // Step j: start K_{j+KAHEAD} (into the buffer of K_{j-1}) and V_{j+VAHEAD}
+    // (into the buffer of V_{j-2}); matrix work on K_j and V_{j-1}; softmax of
+    // S_j.  A work-group with no visible tile (empty sequence, or every row
+    // above the causal diagonal) runs no step: its copies would address tile -1.
+    if (n_kt > 0) {
+      // Step j uses K buffer kb = j % NBUF and V buffer (kb - 1) % NBUF.  The
+      // loop is unrolled by NBUF so that every buffer index is a constant and
+      // the buffer bases fold into the LDS instructions' offset fields.
+      auto step = [&](int j, int kb) {
+        run_groups();  // K_j in K buffer kb, V_{j-1} in V buffer kb-1 (set and preloaded before)
+        // Copies go out after the matrix work is issued: at the start of the
+        // phase all four waves of the group would queue them at once, holding
+        // back their first MFMAs.
+        copy_tile(kg, j + KAHEAD, kv_lds[(kb + KAHEAD) % NBUF], false);
+        copy_tile(vg, j + VAHEAD, kv_lds[NBUF + (kb + VAHEAD) % NBUF], true);
+        wait_mid();
+        barrier();
+        set_bufs((kb + 1) % NBUF, kb);  // step j + 1: K_{j+1} in K buffer kb+1, V_j in V buffer kb
+        preload();                      // (after the last step: harmless reads that nothing uses)
+        softmax_phase(j);
+        wait_end();
+        barrier();
+      };
+      set_bufs(0, NBUF - 1);
+      preload();
+      // (written out: an unrolled loop with an exit test costs the register
+      // allocation some 40 VGPRs)
+      for (int j = 0; j <= n_kt; j += NBUF) {
+        step(j, 0);
+        if (j + 1 > n_kt) break;
+        step(j + 1, 1);
+        if (j + 2 > n_kt) break;
+        step(j + 2, 2);
+        if constexpr (NBUF == 4) {
+          if (j + 3 > n_kt) break;
+          step(j + 3, 3);
+        }
+      }
+    }
+    if (lead) barrier();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the clamped copies before the epilogue
+    // Before the next tile's LDS writes, every wave's copies of this tile
+    // have landed (the last step's may still be in flight at the barrier above).
+    if (ti + 1 < n_tiles_here) barrier();
+
+    const float lt = pair_sum32(l);
+    const float lrt = pair_sum32(lr);
+    if (qrow < nq) {
+      const float inv = lt > 0.f ? 1.f / lrt : 0.f;
+      uint16_t* op = p.o + (q_base + qrow) * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        for (int g = 0; g < 4; ++g) {
+          uint2 w;
+          w.x = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+          w.y = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+          *(uint2*)(op + db * 32 + 8 * g + 4 * hi) = w;
+        }
+      if (hi == 0) p.lse[q_base + qrow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
     }
-    const float m_use = (m == kNegInf) ? 0.f : m;
-    float rsp[4] = {0.f, 0.f, 0.f, 0.f}, lrp[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], p.scale_log2, -m_use));
-        rsp[r & 3] += s[kb][r];
-      }
-    l += (rsp[0] + rsp[1]) + (rsp[2] + rsp[3]);
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        float t[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) t[e] = s[kb][8 * mm + e];
-        pf[kb * 2 + mm] = pack_bf16x8_sum(t, lrp[kb * 2 + mm]);
-      }
-    lr += (lrp[0] + lrp[1]) + (lrp[2] + lrp[3]);
-  };
-
-  // Each step issues exactly four copies per wave (K_{j+2}, V_{j+1}), after
-  // its matrix work.  K_{j+1} and V_j (step j-1's copies) are first read by
-  // the early fragment reads of step j's softmax phase; for group 0 that
-  // phase opens with the barrier in which group 1 ends step j-1.  So every
-  // wave waits for all of its copies (vmcnt 0) before the barrier that ends
-  // its step: a step's copies then have the softmax phase to land, and both
-  // groups' copies of step j-1 are complete before either group reads them.
-  // Before the mid-step barrier a wave only needs the previous step's copies
-  // (vmcnt 4, already true).  The loop body stays free of group-dependent
-  // code, which stops the compiler from cloning it per group.  lgkmcnt(0)
-  // retires this wave's LDS reads before any barrier, so a buffer is free
-  // once the barrier after its last use has passed.
-  auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-  auto wait_copies = [&]() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); };
-  auto wait_all_copies = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-
-  // Step 0 multiplies P = 0 by V buffer 2, which no copy has filled yet:
-  // give it finite contents.
-  for (int i = tid; i < T::TILE / 8; i += T::THREADS) ((uint4*)kv_lds[5])[i] = uint4{0, 0, 0, 0};
-  if (n_kt > 0) {
-    copy_tile(kg, 0, kv_lds[0], false);
-    copy_tile(kg, 1, kv_lds[1], false);
-    copy_tile(vg, 0, kv_lds[3], true);
-    wait_all_copies();  // K_0, K_1 and V_0 are in before either group reads them
-  }
-  barrier();
-  if (!lead) barrier();
-  // Step j: start K_{j+2} (into the buffer of K_{j-1}) and V_{j+1} (into the
-  // buffer of V_{j-2}); matrix work on K_j and V_{j-1}; softmax of S_j.
-  // A work-group with no visible tile (empty sequence, or every row above
-  // the causal diagonal) runs no step: its copies would address tile -1.
-  if (n_kt > 0) {
-    // Step j uses buffers j % 3 (K_j), (j + 2) % 3 (V_{j-1}, then K_{j+2})
-    // and (j + 1) % 3 (V_{j+1}).  The loop is unrolled by three so that every
-    // buffer index is a constant and the buffer bases fold into the LDS
-    // instructions' offset fields.
-    auto step = [&](int j, int b0, int b1, int b2) {
-      run_groups();  // K_j in K buffer b0, V_{j-1} in V buffer b2 (set and preloaded before)
-      // Copies go out after the matrix work is issued: at the start of the
-      // phase all four waves of the group would queue them at once, holding
-      // back their first MFMAs.
-      copy_tile(kg, j + 2, kv_lds[b2], false);
-      copy_tile(vg, j + 1, kv_lds[3 + b1], true);
-      wait_copies();
-      barrier();
-      set_bufs(b1, b0);  // step j + 1: K_{j+1} in K buffer b1, V_j in V buffer b0
-      preload();         // (after the last step: harmless reads that nothing uses)
-      softmax_phase(j);
-      wait_all_copies();
-      barrier();
-    };
-    set_bufs(0, 2);
-    preload();
-    for (int j = 0; j <= n_kt; j += 3) {
-      step(j, 0, 1, 2);
-      if (j + 1 > n_kt) break;
-      step(j + 1, 1, 2, 0);
-      if (j + 2 > n_kt) break;
-      step(j + 2, 2, 0, 1);
-    }
-  }
-  if (lead) barrier();
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the clamped copies before exit
-
-  const float lt = pair_sum32(l);
-  const float lrt = pair_sum32(lr);
-  if (qrow < nq) {
-    const float inv = lt > 0.f ? 1.f / lrt : 0.f;
-    uint16_t* op = p.o + (q_base + qrow) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint2 w;
-        w.x = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
-        w.y = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-        *(uint2*)(op + db * 32 + 8 * g + 4 * hi) = w;
-      }
-    if (hi == 0) p.lse[q_base + qrow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
   }
 }
 
@@ -675,12 +713,13 @@ static FwdParams make_params(const AttnArgs& a, int bm) {
   return p;
 }
 
-template <bool CAUSAL, int MODE>
+template <bool CAUSAL, int MODE, int NBUF = 3, bool PAIR = false>
 static hipError_t launch_fwd_bf16_pp(const AttnArgs& a) {
   const FwdParams p = make_params(a, PPTile::BM);
-  const long long grid = (long long)p.n_qtiles * a.B * a.Hq;
+  const long long slots = PAIR ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
+  const long long grid = slots * a.B * a.Hq;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_pp_kernel<CAUSAL, MODE>), dim3((unsigned)grid), dim3(PPTile::THREADS), 0,
+  hipLaunchKernelGGL((fwd_bf16_pp_kernel<CAUSAL, MODE, NBUF, PAIR>), dim3((unsigned)grid), dim3(PPTile::THREADS), 0,
                      a.stream, p);
   return hipGetLastError();
 }

@@ -1,0 +1,42 @@
+/*
+ * fa_ceilings.h -- measurement aids exported by libfa.so beside the attention
+ * entry points of fa.h.  They measure what the GPU sustains for the two
+ * resources the attention kernels are bound by, so that a kernel's throughput
+ * can be read against a measured ceiling as well as against the published
+ * peak.  Neither is part of the attention path.
+ *
+ * Both enqueue one kernel on `stream` (a hipStream_t, NULL = null stream) and
+ * return 0, -1 for invalid arguments (checked before any HIP call) or -4 if
+ * the launch failed.  Time them with events on the same stream.
+ */
+#ifndef FA_CEILINGS_H_
+#define FA_CEILINGS_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * fa_ceiling_mfma -- `blocks` work-groups of 256 threads (4 waves; two waves
+ * share a SIMD) each issue `iters` x 4 dense bf16 matrix-core products
+ * v_mfma_f32_32x32x16_bf16 (32768 FLOP each) on register operands, in four
+ * independent accumulator chains.  FLOP per launch =
+ * blocks * 4 * iters * 4 * 32768.  out: DEVICE float[blocks * 256], written.
+ */
+int fa_ceiling_mfma(float* out, int blocks, int iters, void* stream);
+
+/*
+ * fa_ceiling_read -- `blocks` work-groups of 256 threads read `bytes` bytes at
+ * `src` (DEVICE, 16-byte aligned, bytes a multiple of 16) once with 16-byte
+ * nontemporal loads, four in flight per lane.  out: DEVICE
+ * unsigned[blocks * 256], written (an xor of what each thread read).
+ */
+int fa_ceiling_read(const void* src, size_t bytes, unsigned* out, int blocks, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_CEILINGS_H_ */

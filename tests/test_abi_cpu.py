@@ -10,15 +10,18 @@ from exact_tiled_attention_08_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
+HEADERS = [HEADER, os.path.join(ROOT, "include", "fa_ceilings.h")]
 
 BAD, UNSUP, WS = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED, _lib.FA_ERR_WORKSPACE
 P = 0x10000  # a 256-byte-aligned fake device address; never dereferenced by these calls
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(fa_\w+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -215,3 +218,11 @@ def test_fp8_rejects(lib, kwargs, status):
 @pytest.mark.parametrize("kwargs", [dict(B=0), dict(Nq=0, q=None, o=None, lse=None), dict(dtype=3, Hq=0)])
 def test_fp8_empty_is_noop(lib, kwargs):
     assert fwd_fp8(lib, **kwargs) == _lib.FA_OK, lib.fa_last_error()
+
+
+def test_ceiling_aids_reject_bad_arguments(lib):
+    assert lib.fa_ceiling_mfma(None, 4, 10, None) == -1
+    assert lib.fa_ceiling_mfma(P, 0, 10, None) == -1
+    assert lib.fa_ceiling_read(P, 17, P, 4, None) == -1
+    assert lib.fa_ceiling_read(P + 4, 32, P, 4, None) == -1
+    assert lib.fa_ceiling_read(None, 32, P, 4, None) == -1

@@ -51,3 +51,18 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_padded_causal_flops_counts_visible_pairs():
+    # row i of sequence b sees keys j <= i with j < L_b (Nq = Nk = N)
+    N, d, H = 37, 64, 3
+    lens = [0, 1, 20, 36, 37, 50]
+    brute = sum(1 for L in lens for i in range(N) for j in range(N) if j <= i and j < min(L, N))
+    assert bench.padded_causal_flops(H, N, lens, d) == 4.0 * d * H * brute
+    assert bench.padded_causal_flops(32, 4096, [4096] * 4, 128) == bench.prefill_flops(4, 32, 4096, 4096, 128, True)
+
+
+def test_stats_of_launch_times():
+    st = bench.stats_ms([5.0, 1.0, 3.0, 2.0, 4.0, 10.0, 6.0, 7.0, 8.0, 9.0])
+    assert st["min_ms"] == 1.0 and st["median_ms"] == 5.5 and st["mean_ms"] == 5.5 and st["p90_ms"] == 9.0
+    assert bench.stats_ms([2.0])["p90_ms"] == 2.0
