@@ -11,9 +11,10 @@ import math
 import torch
 
 from . import _lib
-from ._lib import FAError, FA_DECODE_SPLIT_ALIGN, FA_MAX_SPLITS  # noqa: F401
+from ._lib import FAError, FA_DECODE_SPLIT_ALIGN, FA_MAX_SPLITS, FA_NOALLOC_SCRATCH_BYTES  # noqa: F401
 
 __all__ = ["fa_fwd", "fa_fwd_fp8", "fa_fwd_varlen", "fa_decode_splitkv", "fa_lse_merge", "fa_decode", "fa_decode_workspace_bytes",
+           "fa_decode_noalloc",
            "fa_decode_paged", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_last_error", "FAError",
            "default_scale", "attention"]
 
@@ -265,6 +266,22 @@ def fa_decode(q, k_cache, v_cache, kv_seqlens=None, num_splits=16, scale=None, w
         _lib.check(lib.fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, Hq, Hkv, Nk, d,
                                  s, _ptr(lens), num_splits, _ptr(workspace), workspace.numel(),
                                  _DTYPES[q.dtype], _stream(q)))
+    return out, lse
+
+
+def fa_decode_noalloc(q, k_cache, v_cache, out, lse, kv_seqlens=None, num_splits=16, scale=None):
+    """fa_decode without a workspace, for callers that cannot allocate: the split
+    partials live in the library's static per-GPU scratch (FA_NOALLOC_SCRATCH_BYTES).
+    out [B,Hq,1,d] (q's dtype) and lse [B,Hq,1] float32 are caller-provided;
+    nothing is allocated.  Calls that overlap on one GPU race on the scratch."""
+    B, Hq, Hkv, Nk, d = _decode_shapes(q, k_cache, v_cache)
+    lens = _lens(kv_seqlens, B, q.device)
+    _check_decode_out(out, lse, q)
+    s = default_scale(d) if scale is None else float(scale)
+    lib = _lib.load()
+    with torch.cuda.device(q.device):  # kernels launch on the current device
+        _lib.check(lib.fa_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, Hq, Hkv,
+                                         Nk, d, s, _ptr(lens), num_splits, _DTYPES[q.dtype], _stream(q)))
     return out, lse
 
 

@@ -12,6 +12,7 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0,
 FA_F32, FA_BF16, FA_FP8_E4M3, FA_FP8_E5M2 = 0, 1, 2, 3
 FA_DECODE_SPLIT_ALIGN = 128
 FA_MAX_SPLITS = 256
+FA_NOALLOC_SCRATCH_BYTES = 33554432
 
 _p, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 
@@ -24,6 +25,7 @@ PROTOTYPES = {
     "fa_decode_splitkv": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _i, _i, _p]),
     "fa_lse_merge": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _p]),
     "fa_decode": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _i, _p, _sz, _i, _p]),
+    "fa_decode_noalloc": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _i, _i, _p]),
     "fa_decode_paged": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _i, _p, _sz, _i, _p]),
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "fa_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _p, _sz, _i, _p]),

@@ -263,6 +263,29 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, 
                        dtype, stream);
 }
 
+int fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int Hq,
+                      int Hkv, int Nk, int d, float scale, const int32_t* kv_seqlens, int num_splits, int dtype,
+                      void* stream) {
+  int st = check_decode_args(q, k_cache, v_cache, B, Hq, Hkv, Nk, d, scale, num_splits, dtype);
+  if (st != FA_OK) return st;
+  if ((long long)B * Hq == 0) return ok();
+  if ((st = check_ptr(o, 16, "o")) != FA_OK) return st;
+  if ((st = check_ptr(lse, 4, "lse")) != FA_OK) return st;
+  if (kv_seqlens != nullptr && !aligned(kv_seqlens, 4))
+    return fail(FA_ERR_INVALID_ARG, "kv_seqlens is not 4-byte aligned");
+  const size_t need = fa_decode_workspace_bytes(B, Hq, d, num_splits);
+  if (need > (size_t)FA_NOALLOC_SCRATCH_BYTES)
+    return fail(FA_ERR_WORKSPACE,
+                "fa_decode_noalloc: partials of B=%d Hq=%d d=%d num_splits=%d need %zu bytes, more than the "
+                "%d-byte static scratch; use fa_decode with a workspace",
+                B, Hq, d, num_splits, need, FA_NOALLOC_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  const hipError_t e = fa::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "fa_decode_noalloc: static scratch lookup");
+  return decode_launch(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nk, d, scale, kv_seqlens, num_splits, scratch,
+                       dtype, stream);
+}
+
 
 
 int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table, void* o,

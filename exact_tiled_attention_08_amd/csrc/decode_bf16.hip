@@ -18,6 +18,8 @@
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
+#include <mutex>
+
 namespace fa {
 
 template <int D>
@@ -371,6 +373,36 @@ hipError_t launch_lse_merge(const float* o_part, const float* lse_part, void* o,
                          num_splits, rows);
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Decode scratch for callers that cannot allocate (fa_decode_noalloc): the
+// split partials live in this file-scope device array instead of a caller
+// workspace.  Each GPU holds its own copy for the life of the process.  Host
+// code never uses the array's name as an address: its device address is
+// looked up once per device (with that device current) and cached.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> guard(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace fa

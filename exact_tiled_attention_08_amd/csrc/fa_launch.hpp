@@ -52,6 +52,10 @@ hipError_t launch_decode_splitkv_bf16(const AttnArgs& a, const PartialOut& part,
 hipError_t launch_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
                             int rows, int d, int num_splits, bool out_bf16, hipStream_t stream);
 
+// Device address of the static decode scratch (FA_NOALLOC_SCRATCH_BYTES) on
+// the current device; looked up once per device.
+hipError_t noalloc_scratch(void** ptr);
+
 // FP8 prefill forward (d = 128): q, k, v hold FP8 codes (E4M3, or E5M2 when
 // e5m2 != 0) whose real values are descale * value(code); o is bf16.
 struct Fp8Scales {

@@ -192,6 +192,31 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, 
               int num_splits, void* workspace, size_t workspace_bytes, int dtype, void* stream);
 
 /*
+ * fa_decode_noalloc -- fa_decode for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  It computes exactly what
+ * fa_decode computes, with the same kernels, but keeps the split partials in
+ * a static device array of FA_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on every GPU it runs on until the process ends.  The array's address
+ * on a device is looked up on the first call made with that device current;
+ * the call itself allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).
+ *   Arguments as for fa_decode, without the workspace.
+ *   Errors: FA_ERR_WORKSPACE (before any HIP call) when
+ *   fa_decode_workspace_bytes(B, Hq, d, num_splits) exceeds
+ *   FA_NOALLOC_SCRATCH_BYTES; otherwise as for fa_decode.
+ * Every call on one GPU shares that GPU's array, and the array keeps the last
+ * call's partials (every partial a call reads is first written by the same
+ * call, so nothing needs clearing).  Calls that overlap on one GPU -- on
+ * different streams, or from different threads without ordering -- race on the
+ * array and may return wrong results: serialise them.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES 33554432
+int fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Nk, int d, float scale, const int32_t* kv_seqlens,
+                      int num_splits, int dtype, void* stream);
+
+/*
  * fa_decode_paged -- fa_decode over a paged KV cache.  The pages place the KV
  * cache under page management (PagedAttention) without fixing a layout
  * (Concept note, section "是什么", table of related concepts; Explainer,

@@ -43,6 +43,7 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     assert int(re.search(r"#define FA_DECODE_SPLIT_ALIGN (\d+)", text).group(1)) == _lib.FA_DECODE_SPLIT_ALIGN
     assert int(re.search(r"#define FA_MAX_SPLITS (\d+)", text).group(1)) == _lib.FA_MAX_SPLITS
+    assert int(re.search(r"#define FA_NOALLOC_SCRATCH_BYTES (\d+)", text).group(1)) == _lib.FA_NOALLOC_SCRATCH_BYTES
     for name, val in [("FA_OK", 0), ("FA_ERR_INVALID_ARG", -1), ("FA_ERR_UNSUPPORTED", -2),
                       ("FA_ERR_WORKSPACE", -3), ("FA_ERR_HIP", -4), ("FA_F32", 0), ("FA_BF16", 1),
                       ("FA_FP8_E4M3", 2), ("FA_FP8_E5M2", 3)]:
@@ -218,6 +219,30 @@ def test_fp8_rejects(lib, kwargs, status):
 @pytest.mark.parametrize("kwargs", [dict(B=0), dict(Nq=0, q=None, o=None, lse=None), dict(dtype=3, Hq=0)])
 def test_fp8_empty_is_noop(lib, kwargs):
     assert fwd_fp8(lib, **kwargs) == _lib.FA_OK, lib.fa_last_error()
+
+
+def decode_noalloc(lib, q=P, k=P, v=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Nk=100, d=128, scale=0.1, lens=None,
+                   S=16, dtype=1):
+    return lib.fa_decode_noalloc(q, k, v, o, lse, B, Hq, Hkv, Nk, d, scale, lens, S, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(q=None), BAD), (dict(o=None), BAD), (dict(lse=None), BAD), (dict(o=P + 8), BAD), (dict(lens=P + 2), BAD),
+    (dict(d=96), UNSUP), (dict(S=0), UNSUP), (dict(S=257), UNSUP), (dict(Hq=7), UNSUP), (dict(scale=0.0), BAD),
+    # partials beyond the static scratch: refused before any HIP call
+    (dict(B=64, Hq=32, S=64), WS), (dict(B=4096, Hq=64, S=1), WS),
+])
+def test_decode_noalloc_rejects(lib, kwargs, status):
+    assert decode_noalloc(lib, **kwargs) == status
+    assert lib.fa_last_error() != b""
+
+
+def test_decode_noalloc_limit_matches_workspace_size(lib):
+    # the long decode workload (B=64, Hq=32, d=128, 16 splits) fits the scratch,
+    # four times its splits do not
+    assert lib.fa_decode_workspace_bytes(64, 32, 128, 16) <= _lib.FA_NOALLOC_SCRATCH_BYTES
+    assert lib.fa_decode_workspace_bytes(64, 32, 128, 64) > _lib.FA_NOALLOC_SCRATCH_BYTES
+    assert decode_noalloc(lib, B=0) == _lib.FA_OK and decode_noalloc(lib, Hq=0) == _lib.FA_OK
 
 
 def test_ceiling_aids_reject_bad_arguments(lib):
