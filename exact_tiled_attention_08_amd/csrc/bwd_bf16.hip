@@ -9,14 +9,15 @@
 //     dP_ij = dO_i . V_j
 //     dS_ij = P_ij (dP_ij - D_i),   D_i = dO_i . O_i
 //     dV_j += P_ij dO_i,   dK_j += scale dS_ij Q_i,   dQ_i += scale dS_ij K_j
-// Four launches: D (one dot product per query row), dQ (one work-group per
-// 128-query block streaming 32-key tiles), then dV and dK (one work-group per
-// 128-key block streaming the 32-query tiles of every query head that reads
-// it; one kernel, two parts).  The gradient kernels keep different operands
-// on the lanes -- dQ the queries (as in the forward), dV/dK the keys -- so
-// every product takes its operands straight from the recomputed tiles: no
-// atomics and no extra transposes beyond the ds_read_b64_tr_b16 reads already
-// used by the forward.
+// Three launches: D (one dot product per query row), dQ (one work-group per
+// 128-query block streaming 32-key tiles), then dV and dK together (one
+// work-group per 128-key block streaming the 32-query tiles of every query
+// head that reads it).  The gradient kernels keep different operands on the
+// lanes -- dQ the queries (as in the forward), dV/dK the keys -- so every
+// product takes its operands straight from the recomputed tiles: no atomics
+// (every result is deterministic) and no extra transposes beyond the
+// ds_read_b64_tr_b16 reads already used by the forward.  Per visible (query,
+// key) pair the kernels execute seven products: S and dP in both, dQ, dV, dK.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -232,30 +233,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 }
 
 // ---------------------------------------------------------------------------
-// dV and dK, in two launches of one kernel (PART = 0: dV, PART = 1: dK): 4
-// waves x 32 keys per work-group; 32-query tiles of every query head that
-// reads this KV head.  Per tile and wave, with the keys on the lanes:
-//   S  = Q K^T                  (A: Q rows from LDS, B: K rows)          both parts
-//   P  = 2^(S scale log2(e) - LSE)                                        both parts
-//   dV^T += dO^T P              (A: transposed reads of dO, B: P)         PART 0
-//   dP = dO V^T,  dS = P * (dP - D)
-//   dK^T += Q^T dS              (A: transposed reads of Q, B: dS)         PART 1
-// Splitting the two gradients costs one more product (S is recomputed by
-// both) but halves each launch's accumulators (64 registers), so two or more
-// work-groups share a CU instead of one.  PART 0 keeps the block's K rows in
-// LDS; PART 1 keeps each wave's K rows in registers and the block's V rows in
-// LDS.
-template <int D, bool CAUSAL, bool PADDED, int PART>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int BK = 128, BQ = 32;
-  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[BK * D];  // K (PART 0) or V (PART 1)
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[BQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds[BQ * D];
-  __shared__ __attribute__((aligned(16))) float lse_lds[BQ];
-  __shared__ __attribute__((aligned(16))) float d_lds[BQ];
+// dV and dK in one kernel: 4 waves x 32 keys per work-group (keys on the
+// lanes, as above); 32-query tiles of every query head that reads the block.
+// Per tile and wave, four products:
+//   S  = Q K^T      (A: Q rows from LDS, B: the wave's K rows, kept in VGPRs)
+//   dP = dO V^T     (A: dO rows from LDS, B: the block's V rows from LDS)
+//   P  = 2^(S scale log2(e) - LSE),  dS = P * (dP - D)
+//   dV^T += dO^T P  (A: transposed reads of dO),  dK^T += Q^T dS  (A: Q^T)
+// The Q and dO tiles rotate through two LDS buffers, filled by direct
+// global->LDS copies one tile ahead (rows past the sequence re-read its last
+// row: their LSE is +inf, so they carry no weight); wave 0 stages each tile's
+// LSE and row dots.  One barrier per tile (tests/test_schedule_model.py
+// replays the schedule).  64.5 KiB of LDS and at most 256 VGPRs, so two
+// work-groups share a CU.
+template <int D, bool CAUSAL, bool PADDED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_fused_kernel(BwdParams p) {
+  constexpr int BK = 128, BQ = 32, TQ = BQ * D;
+  constexpr int CPR = D / 8, RPI = 64 / CPR;            // 16-byte chunks per row, rows per 1 KiB copy
+  constexpr int QCOPIES = BQ / RPI / 4;                 // 1 KiB copies per wave per Q (or dO) tile
+  constexpr int VCOPIES = BK / RPI / 4;                 // ... per wave for the block's V rows
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[BK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t qdo_lds[2][2][TQ];  // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float ld_lds[2][2][BQ];         // [buffer][LSE (base 2), row dot]
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, li = lane & 31, hi = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int bh_count = p.B * p.Hkv;
   const int bh = blockIdx.x % bh_count;
   const int kt = (int)(blockIdx.x / bh_count);  // causal: the first key blocks carry the most work
@@ -266,124 +269,163 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   const int kt0 = kt * BK;
   const int diag = p.Nk - p.Nq;
   const size_t kv_base = ((size_t)b * p.Hkv + hk) * (size_t)p.Nk;
-  const int key = kt0 + wave * 32 + li;  // this lane's key (both halves)
-  const int key_end = kt0 + __builtin_amdgcn_readfirstlane(wave) * 32 + 32;  // past this wave's keys
+  const int key = kt0 + wave_u * 32 + li;  // this lane's key
+  const int key_end = kt0 + wave_u * 32 + 32;
 
-  // PART 1: B operand of S from registers -- lane (li, hi) holds K of key
-  // `key`, columns 16*st + 8*hi .. +7 (zeros past the sequence's length).
-  bf16x8 kf[PART == 1 ? D / 16 : 1];
-  if constexpr (PART == 1) {
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st)
-      kf[st] = key < kv_len ? *(const bf16x8*)(p.k + (kv_base + key) * D + 16 * st + 8 * hi) : bf16x8{};
-  }
-  {
-    TileStage<D, BK> st_kv;
-    st_kv.load((PART == 0 ? p.k : p.v) + (kv_base + kt0) * D, kv_len - kt0, tid);
-    st_kv.store(kv_lds, tid);
-  }
-
-  // Query tiles that can see a key of this block: all of them, from the one
-  // holding row kt0 - diag on under the causal mask; none if the block lies
-  // wholly past the sequence's length.
   int qt_first = 0;
   if (CAUSAL) qt_first = max(0, kt0 - diag) / BQ;
   const int n_qt = (p.Nq + BQ - 1) / BQ;
   const int per_head = kt0 < kv_len ? max(0, n_qt - qt_first) : 0;
   const int n_it = per_head * group;
 
-  f32x16 acc[D / 32];  // dV (PART 0) or dK (PART 1), transposed
+  // Copies: lane l of copy c brings row c*RPI + l/CPR, source chunk
+  // (l % CPR) ^ swz(row), to LDS position l % CPR of that row.
+  const int cp_row = lane / CPR, cp_chunk = lane % CPR;
+  auto copy_rows = [&](const uint16_t* src, int row0, int nvalid, int c, uint16_t* dst) {
+    const int r = c * RPI + cp_row;
+    const int rs = min(row0 + r, nvalid - 1) - row0;  // rows past the valid ones re-read the last
+    const int off = (rs * D + ((cp_chunk ^ swz<D>(r)) * 8)) * 2;
+    copy16_to_lds(src + (size_t)row0 * D, off, dst + c * 512);
+  };
+  // Query tile `it`: head hq, rows q0 .. q0 + 31.
+  auto tile_of = [&](int it, int& hq, int& q0) {
+    hq = hk * group + it / per_head;
+    q0 = (qt_first + it % per_head) * BQ;
+  };
+  auto issue_tile = [&](int it, int buf) {
+    int hq, q0;
+    tile_of(it, hq, q0);
+    const size_t rb = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
-
-  TileStage<D, BQ> qst, dost;
-  float lse_r = 0.f, d_r = 0.f;  // staged by threads 0 .. BQ-1
-  auto load_it = [&](int it) {
-    const int hq = hk * group + it / per_head;
-    const int q0 = (qt_first + it % per_head) * BQ;
-    const size_t rb = ((size_t)b * p.Hq + hq) * (size_t)p.Nq + q0;
-    qst.load(p.q + rb * D, p.Nq - q0, tid);
-    dost.load(p.dout + rb * D, p.Nq - q0, tid);
-    if (tid < BQ) {
-      const bool ok = q0 + tid < p.Nq;
-      lse_r = ok ? lse_base2(p.lse[rb + tid]) : __builtin_inff();
-      d_r = ok ? p.rowdot[rb + tid] : 0.f;
+    for (int i = 0; i < QCOPIES; ++i) {
+      const int c = wave_u * QCOPIES + i;
+      copy_rows(p.q + rb * D, q0, p.Nq, c, qdo_lds[buf][0]);
+      copy_rows(p.dout + rb * D, q0, p.Nq, c, qdo_lds[buf][1]);
     }
   };
-  if (n_it > 0) load_it(0);
-  for (int it = 0; it < n_it; ++it) {
-    __syncthreads();
-    qst.store(q_lds, tid);
-    dost.store(do_lds, tid);
-    if (tid < BQ) {
-      lse_lds[tid] = lse_r;
-      d_lds[tid] = d_r;
-    }
-    __syncthreads();
-    const int q0 = (qt_first + it % per_head) * BQ;
-    if (it + 1 < n_it) load_it(it + 1);
+  // Wave 0 loads the tile's LSE (lanes 0..31) and row dots (lanes 32..63).
+  float ld_reg = 0.f;
+  auto load_ld = [&](int it) {
+    int hq, q0;
+    tile_of(it, hq, q0);
+    const size_t rb = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
+    const int q = q0 + li;
+    if (hi == 0) ld_reg = q < p.Nq ? lse_base2(p.lse[rb + q]) : __builtin_inff();
+    else ld_reg = q < p.Nq ? p.rowdot[rb + q] : 0.f;
+  };
 
+  // B operand of S: lane (li, hi) holds K of key `key`, columns 16*st + 8*hi .. +7
+  // (zeros past the sequence's length).
+  bf16x8 kf[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+    kf[st] = key < kv_len ? *(const bf16x8*)(p.k + (kv_base + key) * D + 16 * st + 8 * hi) : bf16x8{};
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) asm volatile("" : "+v"(kf[st]));
+
+  f32x16 acc_dv[D / 32], acc_dk[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc_dv[db] = acc_dk[db] = f32x16{};
+
+  if (n_it > 0) {
+    const uint16_t* vsrc = p.v + kv_base * D;
+#pragma unroll
+    for (int i = 0; i < VCOPIES; ++i) copy_rows(vsrc, kt0, kv_len, wave_u * VCOPIES + i, v_lds);
+    issue_tile(0, 0);
+    if (wave_u == 0) load_ld(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (wave_u == 0) ld_lds[0][hi][li] = ld_reg;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  for (int it = 0; it < n_it; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < n_it) {
+      issue_tile(it + 1, buf ^ 1);
+      if (wave_u == 0) load_ld(it + 1);
+    }
+    int hq_unused, q0;
+    tile_of(it, hq_unused, q0);
+    const uint16_t* qt = qdo_lds[buf][0];
+    const uint16_t* dt = qdo_lds[buf][1];
+
+    // One k-step's fragments at a time (the scheduling barriers keep the
+    // compiler from hoisting every read, which would not fit the register
+    // budget); the other work-group on the SIMD covers the read latency.
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-      const bf16x8 kb = PART == 1 ? kf[st] : *(const bf16x8*)(kv_lds + tile_off<D>(wave * 32 + li, 2 * st + hi));
-      s = mfma32x32x16(*(const bf16x8*)(q_lds + tile_off<D>(li, 2 * st + hi)), kb, s);
-      if constexpr (PART == 1)
-        dp = mfma32x32x16(*(const bf16x8*)(do_lds + tile_off<D>(li, 2 * st + hi)),
-                          *(const bf16x8*)(kv_lds + tile_off<D>(wave * 32 + li, 2 * st + hi)), dp);
+      const bf16x8 fq = *(const bf16x8*)(qt + tile_off<D>(li, 2 * st + hi));
+      const bf16x8 fd = *(const bf16x8*)(dt + tile_off<D>(li, 2 * st + hi));
+      const bf16x8 fv = *(const bf16x8*)(v_lds + tile_off<D>(wave_u * 32 + li, 2 * st + hi));
+      s = mfma32x32x16(fq, kf[st], s);
+      dp = mfma32x32x16(fd, fv, dp);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // lane l: key `key`; register r: query q0 + 8(r/4) + 4*hi + r%4
-    // Tiles whose queries all see every key of the wave skip the per-element
-    // mask (query rows past Nq have LSE +inf, so their P is 0 anyway).
+    // lane l: key `key`; register r: query q0 + 8(r/4) + 4*hi + r%4.  Tiles
+    // whose queries all see every key of the wave skip the per-element mask.
     const bool full = key_end <= kv_len && (!CAUSAL || key_end - 1 <= q0 + diag);
-    float g[16];  // P (PART 0) or dS (PART 1)
-    auto tile_elems = [&](bool masked) {
+    // P and dS for eight queries (registers 8*mm .. 8*mm+7) at a time, packed
+    // to bf16 at once, so only half of them are ever live in float32.
+    bf16x8 pf[2], dsf[2];
+    auto half = [&](int mm, bool masked) {
+      float pv[8], dsv[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 lv = *(const float4*)(lse_lds + 8 * j + 4 * hi);
-        const float lse4[4] = {lv.x, lv.y, lv.z, lv.w};
-        float d4[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (PART == 1) {
-          const float4 dv4 = *(const float4*)(d_lds + 8 * j + 4 * hi);
-          d4[0] = dv4.x; d4[1] = dv4.y; d4[2] = dv4.z; d4[3] = dv4.w;
-        }
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * mm + jj;
+        const float4 l4 = *(const float4*)(&ld_lds[buf][0][8 * j + 4 * hi]);
+        const float4 d4 = *(const float4*)(&ld_lds[buf][1][8 * j + 4 * hi]);
+        const float lse4[4] = {l4.x, l4.y, l4.z, l4.w}, dr4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int r = 4 * j + x;
-          const int q = q0 + 8 * j + 4 * hi + x;
           bool vis = true;
           if (masked) {
+            const int q = q0 + 8 * j + 4 * hi + x;
             vis = key < kv_len && q < p.Nq;
             if (CAUSAL) vis = vis && key <= q + diag;
           }
           const float pr = vis ? fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -lse4[x])) : 0.f;
-          g[r] = PART == 0 ? pr : pr * (dp[r] - d4[x]);
+          pv[4 * jj + x] = pr;
+          dsv[4 * jj + x] = pr * (dp[r] - dr4[x]);
         }
       }
+      pf[mm] = pack_bf16x8(pv);
+      dsf[mm] = pack_bf16x8(dsv);
     };
-    if (full) tile_elems(false);
-    else tile_elems(true);
-    bf16x8 gf[2];
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm) gf[mm] = pack_bf16x8(g + 8 * mm);
-    const uint16_t* a_tile = PART == 0 ? do_lds : q_lds;
+    for (int mm = 0; mm < 2; ++mm) {
+      if (full) half(mm, false);
+      else half(mm, true);
+    }
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) acc[db] = mfma32x32x16(tr_fragment<D>(a_tile, 16 * mm, db, lane), gf[mm], acc[db]);
+      for (int mm = 0; mm < 2; ++mm) {
+        acc_dv[db] = mfma32x32x16(tr_fragment<D>(dt, 16 * mm, db, lane), pf[mm], acc_dv[db]);
+        acc_dk[db] = mfma32x32x16(tr_fragment<D>(qt, 16 * mm, db, lane), dsf[mm], acc_dk[db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next tile's copies and LSE/row dots
+    if (wave_u == 0 && it + 1 < n_it) ld_lds[buf ^ 1][hi][li] = ld_reg;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
   if (key < p.Nk) {
-    uint16_t* op = (PART == 0 ? p.dv : p.dk) + (kv_base + key) * D;
-    const float f = PART == 0 ? 1.f : p.scale;
+    uint16_t* dvp = p.dv + (kv_base + key) * D;
+    uint16_t* dkp = p.dk + (kv_base + key) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         uint2 w;
-        w.x = pack_bf16x2(acc[db][4 * g4] * f, acc[db][4 * g4 + 1] * f);
-        w.y = pack_bf16x2(acc[db][4 * g4 + 2] * f, acc[db][4 * g4 + 3] * f);
-        *(uint2*)(op + db * 32 + 8 * g4 + 4 * hi) = w;
+        w.x = pack_bf16x2(acc_dv[db][4 * g4], acc_dv[db][4 * g4 + 1]);
+        w.y = pack_bf16x2(acc_dv[db][4 * g4 + 2], acc_dv[db][4 * g4 + 3]);
+        *(uint2*)(dvp + db * 32 + 8 * g4 + 4 * hi) = w;
+        w.x = pack_bf16x2(acc_dk[db][4 * g4] * p.scale, acc_dk[db][4 * g4 + 1] * p.scale);
+        w.y = pack_bf16x2(acc_dk[db][4 * g4 + 2] * p.scale, acc_dk[db][4 * g4 + 3] * p.scale);
+        *(uint2*)(dkp + db * 32 + 8 * g4 + 4 * hi) = w;
       }
   }
 }
@@ -417,8 +459,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   if (krows > 0) {
     p.n_tiles = (a.Nk + 127) / 128;
     const dim3 grid((unsigned)((long long)p.n_tiles * a.B * a.Hkv));
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, PADDED, 0>), grid, dim3(256), 0, a.stream, p);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, PADDED, 1>), grid, dim3(256), 0, a.stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_fused_kernel<D, CAUSAL, PADDED>), grid, dim3(256), 0, a.stream, p);
   }
   return hipGetLastError();
 }

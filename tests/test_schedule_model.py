@@ -170,11 +170,13 @@ def check_schedule(writes, reads):
     for c in writes:
         for o in c["owners"]:
             index.setdefault((c["buf"], o), []).append(c)
-    owners = sorted({o for c in writes for o in c["owners"]})
+    owners = {}
+    for c in writes:
+        owners.setdefault(c["buf"], set()).update(c["owners"])
     for r in reads:
         if r["tile"] is None:
             continue
-        for o in owners:
+        for o in sorted(owners.get(r["buf"], ())):
             ws = [c for c in index.get((r["buf"], o), []) if c["issue"] <= r["epoch"]]
             if not ws:
                 errors.append(("never written", r, o))
@@ -363,6 +365,85 @@ def test_sp_schedule_variants_race(bad):
     """Waiting only for the previous step's copies lets the early V reads race;
     one tile more of lookahead overwrites a tile still in use."""
     writes, reads = replay_sp(9, **{**SP_SCHEDULE, **bad})
+    assert check_schedule(writes, reads)
+
+
+# ---------------------------------------------------------------------------
+# The fused dK/dV backward kernel: four waves; the block's V rows are copied
+# once; the Q and dO tiles of iteration t rotate through two buffers.
+# Iteration t first issues the copies of tile t+1 into the other buffer (and
+# wave 0 loads the tile's LSE and row dots into registers), computes on
+# buffer t % 2, waits for all of its loads (vmcnt 0), lets wave 0 store the
+# next LSE/row dots into the other buffer, and ends with a barrier.
+def replay_bwd(n_it, nbuf=2, end_wait=0, ahead=1):
+    n_waves = 4
+    waves = [Wave(w, 0) for w in range(n_waves)]
+    rows = {w: frozenset(range(8 * w, 8 * w + 8)) for w in range(n_waves)}
+    everyone = frozenset(range(32))
+    writes, reads = [], []
+    for w in waves:
+        w.landed, w.lds_pending, w.issued = [], [], []
+
+        def write(buf, tile, owners, lds_store=False, w=w):
+            c = {"issuer": w.wid, "owners": owners, "buf": buf, "tile": tile, "issue": w.epoch, "publish": None,
+                 "idx": len(writes)}
+            writes.append(c)
+            if lds_store:
+                w.lds_pending.append(c)
+            else:
+                w.vm.extend([c, c])
+                w.issued.append(c)
+
+        def wait(n, w=w):
+            w.vm = w.vm[max(0, len(w.vm) - n):]
+            pending = {id(c) for c in w.vm}
+            for c in w.issued:
+                if c["publish"] is None and id(c) not in pending and c not in w.landed:
+                    w.landed.append(c)
+
+        def barrier(w=w):
+            for c in w.landed + w.lds_pending:
+                if c["publish"] is None:
+                    c["publish"] = w.epoch + 1
+            w.landed, w.lds_pending = [], []
+            w.epoch += 1
+
+        def read(buf, tile, w=w):
+            reads.append({"wave": w.wid, "buf": buf, "tile": tile, "epoch": w.epoch})
+
+        if n_it > 0:
+            write(("V",), ("v",), frozenset(range(128 * w.wid // 4, 128 * (w.wid + 1) // 4)))
+            for t in range(ahead):
+                if t < n_it:
+                    write(("QdO", t % nbuf), ("tile", t), rows[w.wid])
+            wait(0)
+            if w.wid == 0:
+                write(("L", 0), ("tile", 0), everyone, lds_store=True)
+        barrier()
+        for t in range(n_it):
+            if t + ahead < n_it:
+                write(("QdO", (t + ahead) % nbuf), ("tile", t + ahead), rows[w.wid])
+            read(("QdO", t % nbuf), ("tile", t))
+            read(("L", t % nbuf), ("tile", t))
+            read(("V",), ("v",))
+            wait(end_wait)
+            if w.wid == 0 and t + 1 < n_it:
+                write(("L", (t + 1) % nbuf), ("tile", t + 1), everyone, lds_store=True)
+            barrier()
+    return writes, reads
+
+
+@pytest.mark.parametrize("n_it", [1, 2, 3, 4, 7, 20])
+def test_bwd_schedule_is_race_free(n_it):
+    writes, reads = replay_bwd(n_it)
+    assert check_schedule(writes, reads) == []
+
+
+@pytest.mark.parametrize("bad", [dict(end_wait=2), dict(ahead=2)])
+def test_bwd_schedule_variants_race(bad):
+    """Leaving the next tile's copies in flight at the barrier, or copying two
+    tiles ahead into a ring of two, lets a read race its copy."""
+    writes, reads = replay_bwd(6, **bad)
     assert check_schedule(writes, reads)
 
 
