@@ -9,8 +9,8 @@
 //     dP_ij = dO_i . V_j
 //     dS_ij = P_ij (dP_ij - D_i),   D_i = dO_i . O_i
 //     dV_j += P_ij dO_i,   dK_j += scale dS_ij Q_i,   dQ_i += scale dS_ij K_j
-// Three launches: D (one dot product per query row), dQ (one work-group per
-// 128-query block streaming 32-key tiles), then dV and dK together (one
+// Two launches: dQ (one work-group per 128-query block streaming 32-key
+// tiles; it also forms the row dots D = dO . O), then dV and dK together (one
 // work-group per 128-key block streaming the 32-query tiles of every query
 // head that reads it).  The gradient kernels keep different operands on the
 // lanes -- dQ the queries (as in the forward), dV/dK the keys -- so every
@@ -30,31 +30,19 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {
   return row * D + ((chunk ^ swz<D>(row)) * 8);
 }
 
-// Register-staged copy of an R-row tile: load() reads rows [0, nvalid) of a
-// row-major [*, D] bf16 tensor (later rows become zeros), store() writes the
-// swizzled tile to LDS.  256 threads; consecutive threads take consecutive
-// 16-byte chunks of a row.
-template <int D, int R>
-struct TileStage {
-  static constexpr int CPR = D / 8;
-  static constexpr int CH = R * CPR / 256;
-  static_assert(CH >= 1 && R * CPR % 256 == 0, "tile must split evenly over 256 threads");
-  uint4 reg[CH];
-  __device__ __forceinline__ void load(const uint16_t* base, int nvalid, int tid) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int idx = tid + c * 256, row = idx / CPR, ch = idx % CPR;
-      reg[c] = row < nvalid ? *(const uint4*)(base + (size_t)row * D + ch * 8) : uint4{0, 0, 0, 0};
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int idx = tid + c * 256, row = idx / CPR, ch = idx % CPR;
-      *(uint4*)(lds + tile_off<D>(row, ch)) = reg[c];
-    }
-  }
-};
+// Direct global->LDS copy c of a [BN, D] bf16 tile (see the prefill kernels):
+// lane l brings row c*RPI + l/CPR of the tensor rows starting at row0, source
+// chunk (l % CPR) ^ swz(row), to LDS position l % CPR of that tile row; rows
+// at or past nvalid re-read row nvalid - 1 (callers guarantee row0 < nvalid).
+template <int D>
+__device__ __forceinline__ void copy_tile_rows(const uint16_t* src, int row0, int nvalid, int c, uint16_t* dst,
+                                               int lane) {
+  constexpr int CPR = D / 8, RPI = 64 / CPR;
+  const int r = c * RPI + lane / CPR;
+  const int rs = min(row0 + r, nvalid - 1) - row0;
+  const int off = (rs * D + (((lane % CPR) ^ swz<D>(r)) * 8)) * 2;
+  copy16_to_lds(src + (size_t)row0 * D, off, dst + c * 512);
+}
 
 // A operand of an MFMA whose rows are the tile's columns (d) and whose k runs
 // over 16 tile rows starting at r0: two ds_read_b64_tr_b16 (rows r0 + tr_r and
@@ -71,38 +59,14 @@ __device__ __forceinline__ bf16x8 tr_fragment(const uint16_t* tile, int r0, int 
                      lds_read_tr16(tile + tile_off<D>(r0 + 8 + tr_r, ch) + tr_in));
 }
 
-// ---------------------------------------------------------------------------
-// D_i = dO_i . O_i (float32), one row per TPR threads.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restrict__ dout,
-                                                          const uint16_t* __restrict__ o, float* __restrict__ rowdot,
-                                                          long long rows) {
-  constexpr int TPR = D / 8;  // threads per row, 8 elements each
-  const long long row = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
-  const int sub = threadIdx.x % TPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const uint4 a = *(const uint4*)(dout + row * D + sub * 8);
-    const uint4 b = *(const uint4*)(o + row * D + sub * 8);
-    const unsigned ua[4] = {a.x, a.y, a.z, a.w}, ub[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      acc = __builtin_fmaf(__uint_as_float(ua[x] << 16), __uint_as_float(ub[x] << 16), acc);
-      acc = __builtin_fmaf(__uint_as_float(ua[x] & 0xffff0000u), __uint_as_float(ub[x] & 0xffff0000u), acc);
-    }
-  }
-#pragma unroll
-  for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (row < rows && sub == 0) rowdot[row] = acc;
-}
-
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
+  const uint16_t* o;
   const float* lse;
-  const float* rowdot;
+  float* rowdot;  // D_i = dO_i . O_i, written by the dQ kernel, read by the dK/dV kernel
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -122,11 +86,15 @@ __device__ __forceinline__ float lse_base2(float lse) { return lse == kNegInf ? 
 //   S^T  = K Q^T,  dP^T = V dO^T           (A: K / V rows from LDS, B: Q / dO in VGPRs)
 //   dS^T = P^T * (dP^T - D)                (P^T recomputed from the LSE)
 //   dQ^T += K^T dS^T                       (A: K^T by transposed reads, B: dS^T)
+// The kernel first forms each of its rows' D = dO . O (and stores it for the
+// dK/dV kernel); K and V tiles rotate through two LDS buffers filled by
+// direct global->LDS copies one tile ahead, one barrier per tile (the
+// schedule of the dK/dV kernel, replayed in tests/test_schedule_model.py).
 template <int D, bool CAUSAL, bool PADDED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BwdParams p) {
-  constexpr int BM = 128, BN = 32;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[BN * D];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdParams p) {
+  constexpr int BM = 128, BN = 32, TK = BN * D;
+  constexpr int RPI = 64 / (D / 8), COPIES = BN / RPI / 4;  // 1 KiB copies per wave per K (or V) tile
+  __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[2][2][TK];  // [buffer][K, V]
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, li = lane & 31, hi = lane >> 5;
@@ -146,51 +114,77 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 
   const size_t qrow_base = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
   const size_t kv_base = ((size_t)b * p.Hkv + hk) * (size_t)p.Nk;
-  const int qrow = q0 + wave * 32 + li;
+  const int qrow = q0 + wave_u * 32 + li;
   const bool row_ok = qrow < p.Nq;
 
+  // Q and dO of this lane's row (columns 16*st + 8*hi .. +7), and the row's
+  // D = dO . O from the same half rows and the partner lane's.
   bf16x8 qf[D / 16], dof[D / 16];
+  float dpart = 0.f;
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) {
     if (row_ok) {
-      qf[st] = *(const bf16x8*)(p.q + (qrow_base + qrow) * D + 16 * st + 8 * hi);
-      dof[st] = *(const bf16x8*)(p.dout + (qrow_base + qrow) * D + 16 * st + 8 * hi);
+      const size_t off = (qrow_base + qrow) * D + 16 * st + 8 * hi;
+      qf[st] = *(const bf16x8*)(p.q + off);
+      dof[st] = *(const bf16x8*)(p.dout + off);
+      const bf16x8 of = *(const bf16x8*)(p.o + off);
+      const uint4 ud = __builtin_bit_cast(uint4, dof[st]), uo = __builtin_bit_cast(uint4, of);
+      const unsigned d4[4] = {ud.x, ud.y, ud.z, ud.w}, o4[4] = {uo.x, uo.y, uo.z, uo.w};
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        dpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d4[x]), __builtin_bit_cast(bf16x2, o4[x]),
+                                                dpart, false);
     } else {
       qf[st] = bf16x8{};
       dof[st] = bf16x8{};
     }
   }
+  const float drow = pair_sum32(dpart);
+  if (row_ok && hi == 0) p.rowdot[qrow_base + qrow] = drow;
   const float lse2 = row_ok ? lse_base2(p.lse[qrow_base + qrow]) : __builtin_inff();
-  const float drow = row_ok ? p.rowdot[qrow_base + qrow] : 0.f;
 
   f32x16 dq_acc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dq_acc[db] = f32x16{};
 
-  TileStage<D, BN> kst, vst;
   const uint16_t* kg = p.k + kv_base * D;
   const uint16_t* vg = p.v + kv_base * D;
-  if (n_kt > 0) {
-    kst.load(kg, kv_len, tid);
-    vst.load(vg, kv_len, tid);
-  }
-  for (int t = 0; t < n_kt; ++t) {
-    __syncthreads();
-    kst.store(k_lds, tid);
-    vst.store(v_lds, tid);
-    __syncthreads();
-    if (t + 1 < n_kt) {
-      const int k1 = (t + 1) * BN;
-      kst.load(kg + (size_t)k1 * D, kv_len - k1, tid);
-      vst.load(vg + (size_t)k1 * D, kv_len - k1, tid);
+  auto issue = [&](int t, int buf) {
+#pragma unroll
+    for (int i = 0; i < COPIES; ++i) {
+      const int c = wave_u * COPIES + i;
+      copy_tile_rows<D>(kg, t * BN, kv_len, c, kv_lds[buf][0], lane);
+      copy_tile_rows<D>(vg, t * BN, kv_len, c, kv_lds[buf][1], lane);
     }
+  };
+  if (n_kt > 0) {
+    issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  for (int t = 0; t < n_kt; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_kt) issue(t + 1, buf ^ 1);
+    const uint16_t* kl = kv_lds[buf][0];
+    const uint16_t* vl = kv_lds[buf][1];
     const int k0 = t * BN;
 
+    // Fragments are read one k-step (one d-block below) ahead; the
+    // scheduling barriers keep the compiler from hoisting every read.
     f32x16 s = f32x16{}, dp = f32x16{};
+    bf16x8 fk[2], fv[2];
+    fk[0] = *(const bf16x8*)(kl + tile_off<D>(li, hi));
+    fv[0] = *(const bf16x8*)(vl + tile_off<D>(li, hi));
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-      s = mfma32x32x16(*(const bf16x8*)(k_lds + tile_off<D>(li, 2 * st + hi)), qf[st], s);
-      dp = mfma32x32x16(*(const bf16x8*)(v_lds + tile_off<D>(li, 2 * st + hi)), dof[st], dp);
+      if (st + 1 < D / 16) {
+        fk[(st + 1) & 1] = *(const bf16x8*)(kl + tile_off<D>(li, 2 * (st + 1) + hi));
+        fv[(st + 1) & 1] = *(const bf16x8*)(vl + tile_off<D>(li, 2 * (st + 1) + hi));
+      }
+      s = mfma32x32x16(fk[st & 1], qf[st], s);
+      dp = mfma32x32x16(fv[st & 1], dof[st], dp);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // lane l: query qrow; register r: key k0 + 8(r/4) + 4*hi + r%4.  Tiles
     // whose keys are all valid and visible to every row of the wave skip the
@@ -212,10 +206,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     bf16x8 dsf[2];
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm) dsf[mm] = pack_bf16x8(ds + 8 * mm);
+    // Key slice mm outermost: consecutive products accumulate into different
+    // d-blocks (a product that waits for the previous one's accumulator
+    // stalls the matrix core).
+    constexpr int NF = 2 * (D / 32);
+    bf16x8 kt[2];
+    kt[0] = tr_fragment<D>(kl, 0, 0, lane);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) dq_acc[db] = mfma32x32x16(tr_fragment<D>(k_lds, 16 * mm, db, lane), dsf[mm], dq_acc[db]);
+    for (int f = 0; f < NF; ++f) {
+      const int mm = f / (D / 32), db = f % (D / 32);
+      if (f + 1 < NF) kt[(f + 1) & 1] = tr_fragment<D>(kl, 16 * ((f + 1) / (D / 32)), (f + 1) % (D / 32), lane);
+      dq_acc[db] = mfma32x32x16(kt[f & 1], dsf[mm], dq_acc[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next tile's copies
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
   if (row_ok) {
@@ -234,27 +239,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 
 // ---------------------------------------------------------------------------
 // dV and dK in one kernel: 4 waves x 32 keys per work-group (keys on the
-// lanes, as above); 32-query tiles of every query head that reads the block.
-// Per tile and wave, four products:
+// lanes); 32-query tiles of every query head that reads the block.  Per tile
+// and wave, four products:
 //   S  = Q K^T      (A: Q rows from LDS, B: the wave's K rows, kept in VGPRs)
-//   dP = dO V^T     (A: dO rows from LDS, B: the block's V rows from LDS)
+//   dP = dO V^T     (A: dO rows from LDS, B: the wave's V rows from LDS)
 //   P  = 2^(S scale log2(e) - LSE),  dS = P * (dP - D)
 //   dV^T += dO^T P  (A: transposed reads of dO),  dK^T += Q^T dS  (A: Q^T)
 // The Q and dO tiles rotate through two LDS buffers, filled by direct
 // global->LDS copies one tile ahead (rows past the sequence re-read its last
 // row: their LSE is +inf, so they carry no weight); wave 0 stages each tile's
 // LSE and row dots.  One barrier per tile (tests/test_schedule_model.py
-// replays the schedule).  64.5 KiB of LDS and at most 256 VGPRs, so two
-// work-groups share a CU.
+// replays the schedule).  The per-lane LDS offsets are computed once and the
+// (head, query tile) walk advances by counters, so a tile costs no divisions.
+// 64.5 KiB of LDS and at most 256 VGPRs, so two work-groups share a CU.
 template <int D, bool CAUSAL, bool PADDED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_fused_kernel(BwdParams p) {
   constexpr int BK = 128, BQ = 32, TQ = BQ * D;
-  constexpr int CPR = D / 8, RPI = 64 / CPR;            // 16-byte chunks per row, rows per 1 KiB copy
-  constexpr int QCOPIES = BQ / RPI / 4;                 // 1 KiB copies per wave per Q (or dO) tile
-  constexpr int VCOPIES = BK / RPI / 4;                 // ... per wave for the block's V rows
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[BK * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t qdo_lds[2][2][TQ];  // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float ld_lds[2][2][BQ];         // [buffer][LSE (base 2), row dot]
+  constexpr int RPI = 64 / (D / 8);
+  constexpr int QCOPIES = BQ / RPI / 4;  // 1 KiB copies per wave per Q (or dO) tile
+  constexpr int VCOPIES = BK / RPI / 4;  // ... per wave for the block's V rows
+  // LDS (elements): V rows [0, BK*D); Q, dO of buffer 0; Q, dO of buffer 1.
+  constexpr int V_OFF = 0, QDO_OFF = BK * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[BK * D + 4 * TQ];
+  __shared__ __attribute__((aligned(16))) float ld_lds[2][2][BQ];  // [buffer][LSE (base 2), row dot]
+  auto q_off = [](int buf) { return QDO_OFF + 2 * buf * TQ; };
+  auto do_off = [](int buf) { return QDO_OFF + (2 * buf + 1) * TQ; };
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, li = lane & 31, hi = lane >> 5;
@@ -278,40 +287,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int per_head = kt0 < kv_len ? max(0, n_qt - qt_first) : 0;
   const int n_it = per_head * group;
 
-  // Copies: lane l of copy c brings row c*RPI + l/CPR, source chunk
-  // (l % CPR) ^ swz(row), to LDS position l % CPR of that row.
-  const int cp_row = lane / CPR, cp_chunk = lane % CPR;
-  auto copy_rows = [&](const uint16_t* src, int row0, int nvalid, int c, uint16_t* dst) {
-    const int r = c * RPI + cp_row;
-    const int rs = min(row0 + r, nvalid - 1) - row0;  // rows past the valid ones re-read the last
-    const int off = (rs * D + ((cp_chunk ^ swz<D>(r)) * 8)) * 2;
-    copy16_to_lds(src + (size_t)row0 * D, off, dst + c * 512);
+  // Per-lane LDS offsets (elements), computed once; the empty asm keeps the
+  // compiler from recomputing them at every use.  Rows of a tile: row li (row 32*wave + li of the V rows),
+  // chunk 2*st + hi.  Transposed reads: rows tr_r + 8u, chunk 4*db + tr_cc
+  // (rows 16 on share the swizzle).
+  int rd[D / 16], vrd[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    rd[st] = tile_off<D>(li, 2 * st + hi);
+    vrd[st] = V_OFF + tile_off<D>(wave_u * 32 + li, 2 * st + hi);
+  }
+  const int tr_r = 4 * hi + ((lane & 15) >> 2), tr_cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  int tro[D / 32][2];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) tro[db][u] = tile_off<D>(tr_r + 8 * u, 4 * db + tr_cc) + 4 * (lane & 1);
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) asm volatile("" : "+v"(rd[st]), "+v"(vrd[st]));
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) asm volatile("" : "+v"(tro[db][0]), "+v"(tro[db][1]));
+  auto frag = [&](int base, int off) { return *(const bf16x8*)(lds + base + off); };
+  auto tfrag = [&](int base, int mm, int db) {
+    return join_bf16x8(lds_read_tr16(lds + base + 16 * mm * D + tro[db][0]),
+                       lds_read_tr16(lds + base + 16 * mm * D + tro[db][1]));
   };
-  // Query tile `it`: head hq, rows q0 .. q0 + 31.
-  auto tile_of = [&](int it, int& hq, int& q0) {
-    hq = hk * group + it / per_head;
-    q0 = (qt_first + it % per_head) * BQ;
-  };
-  auto issue_tile = [&](int it, int buf) {
-    int hq, q0;
-    tile_of(it, hq, q0);
+
+  // The query tiles in order: head hq = hk*group + h, tile qt_first .. n_qt-1.
+  // (next_h, next_qt) walk them one ahead of the compute.
+  int next_h = 0, next_qt = qt_first;
+  auto issue_next = [&](int buf) {
+    const int hq = hk * group + next_h, q0 = next_qt * BQ;
     const size_t rb = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
 #pragma unroll
     for (int i = 0; i < QCOPIES; ++i) {
       const int c = wave_u * QCOPIES + i;
-      copy_rows(p.q + rb * D, q0, p.Nq, c, qdo_lds[buf][0]);
-      copy_rows(p.dout + rb * D, q0, p.Nq, c, qdo_lds[buf][1]);
+      copy_tile_rows<D>(p.q + rb * D, q0, p.Nq, c, lds + q_off(buf), lane);
+      copy_tile_rows<D>(p.dout + rb * D, q0, p.Nq, c, lds + do_off(buf), lane);
     }
-  };
-  // Wave 0 loads the tile's LSE (lanes 0..31) and row dots (lanes 32..63).
-  float ld_reg = 0.f;
-  auto load_ld = [&](int it) {
-    int hq, q0;
-    tile_of(it, hq, q0);
-    const size_t rb = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
-    const int q = q0 + li;
-    if (hi == 0) ld_reg = q < p.Nq ? lse_base2(p.lse[rb + q]) : __builtin_inff();
-    else ld_reg = q < p.Nq ? p.rowdot[rb + q] : 0.f;
+    // wave 0 loads the tile's LSE (lanes 0..31) and row dots (lanes 32..63)
+    float r = 0.f;
+    if (wave_u == 0) {
+      const int q = q0 + li;
+      if (hi == 0) r = q < p.Nq ? lse_base2(p.lse[rb + q]) : __builtin_inff();
+      else r = q < p.Nq ? p.rowdot[rb + q] : 0.f;
+    }
+    if (++next_qt == n_qt) {
+      next_qt = qt_first;
+      ++next_h;
+    }
+    return r;
   };
 
   // B operand of S: lane (li, hi) holds K of key `key`, columns 16*st + 8*hi .. +7
@@ -327,40 +352,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc_dv[db] = acc_dk[db] = f32x16{};
 
+  float ld_reg = 0.f;
   if (n_it > 0) {
     const uint16_t* vsrc = p.v + kv_base * D;
 #pragma unroll
-    for (int i = 0; i < VCOPIES; ++i) copy_rows(vsrc, kt0, kv_len, wave_u * VCOPIES + i, v_lds);
-    issue_tile(0, 0);
-    if (wave_u == 0) load_ld(0);
+    for (int i = 0; i < VCOPIES; ++i) copy_tile_rows<D>(vsrc, kt0, kv_len, wave_u * VCOPIES + i, lds + V_OFF, lane);
+    ld_reg = issue_next(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (wave_u == 0) ld_lds[0][hi][li] = ld_reg;
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  for (int it = 0; it < n_it; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < n_it) {
-      issue_tile(it + 1, buf ^ 1);
-      if (wave_u == 0) load_ld(it + 1);
-    }
-    int hq_unused, q0;
-    tile_of(it, hq_unused, q0);
-    const uint16_t* qt = qdo_lds[buf][0];
-    const uint16_t* dt = qdo_lds[buf][1];
+  int cur_qt = qt_first;  // query tile being computed
+  // One tile on buffer `buf` (a constant after unrolling).
+  auto tile = [&](int it, int buf) {
+    if (it + 1 < n_it) ld_reg = issue_next(buf ^ 1);
+    const int q0 = cur_qt * BQ;
+    if (++cur_qt == n_qt) cur_qt = qt_first;
 
-    // One k-step's fragments at a time (the scheduling barriers keep the
-    // compiler from hoisting every read, which would not fit the register
-    // budget); the other work-group on the SIMD covers the read latency.
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-      const bf16x8 fq = *(const bf16x8*)(qt + tile_off<D>(li, 2 * st + hi));
-      const bf16x8 fd = *(const bf16x8*)(dt + tile_off<D>(li, 2 * st + hi));
-      const bf16x8 fv = *(const bf16x8*)(v_lds + tile_off<D>(wave_u * 32 + li, 2 * st + hi));
-      s = mfma32x32x16(fq, kf[st], s);
-      dp = mfma32x32x16(fd, fv, dp);
-      __builtin_amdgcn_sched_barrier(0);
+      s = mfma32x32x16(frag(q_off(buf), rd[st]), kf[st], s);
+      dp = mfma32x32x16(frag(do_off(buf), rd[st]), frag(0, vrd[st]), dp);
     }
     // lane l: key `key`; register r: query q0 + 8(r/4) + 4*hi + r%4.  Tiles
     // whose queries all see every key of the wave skip the per-element mask.
@@ -398,19 +412,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (full) half(mm, false);
       else half(mm, true);
     }
+    // Query slice mm outermost: consecutive products accumulate into
+    // different registers (a product that waits for the previous one's
+    // accumulator stalls the matrix core).
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        acc_dv[db] = mfma32x32x16(tr_fragment<D>(dt, 16 * mm, db, lane), pf[mm], acc_dv[db]);
-        acc_dk[db] = mfma32x32x16(tr_fragment<D>(qt, 16 * mm, db, lane), dsf[mm], acc_dk[db]);
+      for (int db = 0; db < D / 32; ++db) {
+        acc_dv[db] = mfma32x32x16(tfrag(do_off(buf), mm, db), pf[mm], acc_dv[db]);
+        acc_dk[db] = mfma32x32x16(tfrag(q_off(buf), mm, db), dsf[mm], acc_dk[db]);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next tile's copies and LSE/row dots
     if (wave_u == 0 && it + 1 < n_it) ld_lds[buf ^ 1][hi][li] = ld_reg;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  }
+  };
+  for (int it = 0; it < n_it; ++it) tile(it, it & 1);
 
   if (key < p.Nk) {
     uint16_t* dvp = p.dv + (kv_base + key) * D;
@@ -446,11 +462,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
+  p.o = (const uint16_t*)a.o;
   const long long rows = (long long)a.B * a.Hq * a.Nq;
-  if (rows > 0) {
-    constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, a.stream,
-                       (const uint16_t*)a.dout, (const uint16_t*)a.o, a.rowdot, rows);
+  if (rows > 0) {  // dQ (and the row dots D the dK/dV kernel reads)
     p.n_tiles = (a.Nq + 127) / 128;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PADDED>), dim3((unsigned)((long long)p.n_tiles * a.B * a.Hq)),
                        dim3(256), 0, a.stream, p);
