@@ -364,11 +364,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   int cur_qt = qt_first;  // query tile being computed
-  // One tile on buffer `buf` (a constant after unrolling).
   auto tile = [&](int it, int buf) {
     if (it + 1 < n_it) ld_reg = issue_next(buf ^ 1);
     const int q0 = cur_qt * BQ;
     if (++cur_qt == n_qt) cur_qt = qt_first;
+    // Tiles whose queries all see every key of the wave skip the mask.
+    const bool masked = !(key_end <= kv_len && (!CAUSAL || key_end - 1 <= q0 + diag));
 
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -376,14 +377,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       s = mfma32x32x16(frag(q_off(buf), rd[st]), kf[st], s);
       dp = mfma32x32x16(frag(do_off(buf), rd[st]), frag(0, vrd[st]), dp);
     }
-    // lane l: key `key`; register r: query q0 + 8(r/4) + 4*hi + r%4.  Tiles
-    // whose queries all see every key of the wave skip the per-element mask.
-    const bool full = key_end <= kv_len && (!CAUSAL || key_end - 1 <= q0 + diag);
-    // P and dS for eight queries (registers 8*mm .. 8*mm+7) at a time, packed
-    // to bf16 at once, so only half of them are ever live in float32.
-    bf16x8 pf[2], dsf[2];
-    auto half = [&](int mm, bool masked) {
-      float pv[8], dsv[8];
+    // lane l: key `key`; register r: query q0 + 8(r/4) + 4*hi + r%4.  P and
+    // dS for eight queries (registers 8*mm .. 8*mm+7) at a time, so only
+    // half of them are ever live in float32.  The exponential runs for every
+    // element (masked-out ones are finite here -- zero K rows, re-read Q rows
+    // -- or have LSE +inf); masked tiles then zero what is not visible, in a
+    // branch of their own so the common path stays one straight-line block.
+    auto half = [&](int mm, float (&pv)[8], float (&dsv)[8]) {
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int j = 2 * mm + jj;
@@ -393,35 +393,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int r = 4 * j + x;
-          bool vis = true;
-          if (masked) {
-            const int q = q0 + 8 * j + 4 * hi + x;
-            vis = key < kv_len && q < p.Nq;
-            if (CAUSAL) vis = vis && key <= q + diag;
-          }
-          const float pr = vis ? fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -lse4[x])) : 0.f;
+          const float pr = fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -lse4[x]));
           pv[4 * jj + x] = pr;
           dsv[4 * jj + x] = pr * (dp[r] - dr4[x]);
         }
       }
-      pf[mm] = pack_bf16x8(pv);
-      dsf[mm] = pack_bf16x8(dsv);
+      if (masked) {
+        // Element e holds query q0 + 4*hi + c with c = 8*(2mm + e/4) + e%4,
+        // visible iff lo <= c < hi_q (lo from the causal diagonal, hi_q from
+        // the query count; an empty range for keys past the sequence).  The
+        // empty asm keeps this a branch taken by masked tiles only.
+        asm volatile("");
+        int lo = CAUSAL ? key - diag - 4 * hi - q0 : INT_MIN / 2;
+        int hi_q = p.Nq - q0 - 4 * hi;
+        if (key >= kv_len) hi_q = lo;
+        const unsigned range = (unsigned)(hi_q - lo);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = 8 * (2 * mm + e / 4) + e % 4;
+          const bool vis = (unsigned)(c - lo) < range && hi_q > lo;
+          pv[e] = vis ? pv[e] : 0.f;
+          dsv[e] = vis ? dsv[e] : 0.f;
+        }
+      }
     };
-#pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      if (full) half(mm, false);
-      else half(mm, true);
-    }
-    // Query slice mm outermost: consecutive products accumulate into
-    // different registers (a product that waits for the previous one's
-    // accumulator stalls the matrix core).
-#pragma unroll
-    for (int mm = 0; mm < 2; ++mm)
+    auto grads = [&](int mm, bf16x8 pf, bf16x8 dsf) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        acc_dv[db] = mfma32x32x16(tfrag(do_off(buf), mm, db), pf[mm], acc_dv[db]);
-        acc_dk[db] = mfma32x32x16(tfrag(q_off(buf), mm, db), dsf[mm], acc_dk[db]);
+        acc_dv[db] = mfma32x32x16(tfrag(do_off(buf), mm, db), pf, acc_dv[db]);
+        acc_dk[db] = mfma32x32x16(tfrag(q_off(buf), mm, db), dsf, acc_dk[db]);
       }
+    };
+    float pv[8], dsv[8];
+    half(0, pv, dsv);
+    const bf16x8 pf0 = pack_bf16x8(pv), dsf0 = pack_bf16x8(dsv);
+    // The first half's dV/dK products and the forming of the second half
+    // share one straight-line block, so they can overlap.
+    grads(0, pf0, dsf0);
+    half(1, pv, dsv);
+    grads(1, pack_bf16x8(pv), pack_bf16x8(dsv));
+
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next tile's copies and LSE/row dots
     if (wave_u == 0 && it + 1 < n_it) ld_lds[buf ^ 1][hi][li] = ld_reg;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
