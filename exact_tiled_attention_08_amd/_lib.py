@@ -33,7 +33,7 @@ PROTOTYPES = {
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_version": (_i, []),
     # measurement aids (include/fa_ceilings.h)
-    "fa_ceiling_mfma": (_i, [_p, _i, _i, _p]),
+    "fa_ceiling_mfma": (_i, [_p, _p, _i, _i, _p]),
     "fa_ceiling_read": (_i, [_p, _sz, _p, _i, _p]),
 }
 

@@ -3,7 +3,9 @@
 //
 //  * ceiling_mfma_kernel: nothing but v_mfma_f32_32x32x16_bf16 on register
 //    operands, four independent accumulator chains per wave, two waves per
-//    SIMD -- the matrix-core rate the prefill can at best approach.
+//    SIMD -- the matrix-core rate the prefill can at best approach.  The rate
+//    depends on the data: on random operands the chip holds a lower clock
+//    than on small constants (power), so both are measured.
 //  * ceiling_read_kernel: a streaming read of a large buffer with 16-byte
 //    nontemporal loads, four in flight per lane -- the HBM rate the decode can
 //    at best approach.
@@ -17,23 +19,36 @@
 
 namespace fa {
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ceiling_mfma_kernel(float* out,
-                                                                                                   int iters) {
+// Each wave holds eight A and eight B fragments and cycles through them, so
+// the operands change from product to product as they do in a real kernel.
+// With `src` they are random bf16 values; without, small constants (few bits
+// toggle, so the matrix cores draw far less power and the clock stays high).
+template <bool DATA>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ceiling_mfma_kernel(
+    const bf16x8* __restrict__ src, float* out, int iters) {
   const int tid = threadIdx.x;
-  // Operands depend on the thread so nothing folds; values stay tiny so the
-  // accumulators never overflow.
-  bf16x8 a, b;
+  bf16x8 a[8], b[8];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    a[t] = (__bf16)((float)((tid + t) & 7) * 0.0078125f);
-    b[t] = (__bf16)((float)((tid * 3 + t) & 7) * 0.0078125f);
+  for (int u = 0; u < 8; ++u) {
+    if (DATA) {
+      a[u] = src[((size_t)blockIdx.x * 16 + u) * 256 + tid];
+      b[u] = src[((size_t)blockIdx.x * 16 + 8 + u) * 256 + tid];
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        a[u][t] = (__bf16)((float)((tid + t + u) & 7) * 0.0078125f);
+        b[u][t] = (__bf16)((float)((tid * 3 + t + u) & 7) * 0.0078125f);
+      }
+    }
   }
   f32x16 acc[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) acc[c] = f32x16{};
   for (int i = 0; i < iters; ++i) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = mfma32x32x16(a, b, acc[c]);
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = mfma32x32x16(a[u], b[(u + c) & 7], acc[c]);
   }
   float s = 0.f;
 #pragma unroll
@@ -66,9 +81,14 @@ __global__ __launch_bounds__(256) void ceiling_read_kernel(const u32x4* __restri
 
 extern "C" {
 
-int fa_ceiling_mfma(float* out, int blocks, int iters, void* stream) {
-  if (out == nullptr || blocks < 1 || iters < 1) return -1;
-  hipLaunchKernelGGL(fa::ceiling_mfma_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
+int fa_ceiling_mfma(const void* src, float* out, int blocks, int iters, void* stream) {
+  if (out == nullptr || blocks < 1 || iters < 1 || ((uintptr_t)src % 16) != 0) return -1;
+  if (src != nullptr)
+    hipLaunchKernelGGL(fa::ceiling_mfma_kernel<true>, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const fa::bf16x8*)src, out, iters);
+  else
+    hipLaunchKernelGGL(fa::ceiling_mfma_kernel<false>, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const fa::bf16x8*)nullptr, out, iters);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

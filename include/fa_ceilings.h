@@ -20,12 +20,16 @@ extern "C" {
 
 /*
  * fa_ceiling_mfma -- `blocks` work-groups of 256 threads (4 waves; two waves
- * share a SIMD) each issue `iters` x 4 dense bf16 matrix-core products
+ * share a SIMD) each issue `iters` x 32 dense bf16 matrix-core products
  * v_mfma_f32_32x32x16_bf16 (32768 FLOP each) on register operands, in four
- * independent accumulator chains.  FLOP per launch =
- * blocks * 4 * iters * 4 * 32768.  out: DEVICE float[blocks * 256], written.
+ * independent accumulator chains, cycling through eight A and eight B
+ * fragments per lane.  FLOP per launch = blocks * 4 * iters * 32 * 32768.
+ * src: DEVICE bf16 operands, blocks * 16 * 256 * 8 values (16-byte aligned),
+ * read once at the start -- random values draw the power real operands
+ * draw, and the sustained clock (so the rate) depends on it -- or NULL for
+ * small constant operands.  out: DEVICE float[blocks * 256], written.
  */
-int fa_ceiling_mfma(float* out, int blocks, int iters, void* stream);
+int fa_ceiling_mfma(const void* src, float* out, int blocks, int iters, void* stream);
 
 /*
  * fa_ceiling_read -- `blocks` work-groups of 256 threads read `bytes` bytes at

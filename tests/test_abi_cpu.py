@@ -246,8 +246,10 @@ def test_decode_noalloc_limit_matches_workspace_size(lib):
 
 
 def test_ceiling_aids_reject_bad_arguments(lib):
-    assert lib.fa_ceiling_mfma(None, 4, 10, None) == -1
-    assert lib.fa_ceiling_mfma(P, 0, 10, None) == -1
+    assert lib.fa_ceiling_mfma(None, None, 4, 10, None) == -1
+    assert lib.fa_ceiling_mfma(None, P, 0, 10, None) == -1
+    assert lib.fa_ceiling_mfma(None, P, 4, 0, None) == -1
+    assert lib.fa_ceiling_mfma(P + 8, P, 4, 10, None) == -1
     assert lib.fa_ceiling_read(P, 17, P, 4, None) == -1
     assert lib.fa_ceiling_read(P + 4, 32, P, 4, None) == -1
     assert lib.fa_ceiling_read(None, 32, P, 4, None) == -1
