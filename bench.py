@@ -430,7 +430,8 @@ def main():
             fl = prefill_flops(c2["B"], c2["Hq"], c2["Nq"], c2["Nk"], c2["d"], causal)
             name = "causal" if causal else "non_causal"
             side["prefill_d64"][name] = mfma_leg(
-                ms, fl, f"fwd_bf16_kernel<64,{'causal' if causal else 'non-causal'}>",
+                ms, fl, "fwd_bf16_kernel<64,causal> (256 ping-pong work-groups would not fill two per CU)"
+                if causal else "fwd_bf16_pp_kernel<64,non-causal>",
                 f"prefill fwd B=2 H=16 N=2048 d=64 {'causal' if causal else 'non-causal'} bf16", mfma_ceiling)
             log(f"d64 {name}: {side['prefill_d64'][name]['value']} TFLOP/s")
         del q2, k2, v2, o2, l2

@@ -10,8 +10,14 @@
 // many work-groups (one per query block) is the grid; the saiita.com.cn
 // explainer, section "二代和三代", credits it for the utilisation gain.
 //
-// Work-group: 4 waves x 32 query rows = 128 rows.  Each KV tile holds 64
-// keys.  Everything per query row lives in one lane pair (lanes i and i+32):
+// Two kernels.  The ping-pong kernel (fwd_bf16_pp_kernel, below) runs d = 128
+// and d = 64; the 4-wave kernel that follows here runs d = 64 under a causal
+// mask when the grid is too small for 256-row work-groups to balance (see
+// launch_mode).
+//
+// 4-wave kernel: 4 waves x 32 query rows = 128 rows per work-group.  Each KV
+// tile holds 64 keys.  In both kernels everything per query row lives in one
+// lane pair (lanes i and i+32):
 //   S^T = K Q^T      A = K rows from LDS, B = Q^T kept in VGPRs
 //   O^T += V^T P^T   A = V^T via ds_read_b64_tr_b16, B = P^T straight from
 //                    the S^T accumulators (rounded to bf16)
@@ -25,6 +31,8 @@
 // __shared__ arrays and the tile loop is unrolled by two, so every LDS read
 // names its buffer statically and the compiler can tell the in-flight copies
 // into the other buffer do not alias it (otherwise it waits for them).
+#include <atomic>
+
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -315,7 +323,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 }
 
 // ---------------------------------------------------------------------------
-// d = 128: eight waves in two groups of four, kept one phase apart ("ping
+// Ping-pong kernel: eight waves in two groups of four, kept one phase apart ("ping
 // pong").  Waves w and w+4 share a SIMD.  In every phase one group runs its
 // matrix-core work for tile j -- S_j = K_j Q^T and O += V_{j-1} P_{j-1} -- while
 // the other group runs the online-softmax update of its previous tile on the
@@ -335,17 +343,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 // Under a causal mask query tile i sees i+1 times the keys of tile 0; with
 // PAIR a work-group runs tile i and then tile n-1-i, so every work-group of a
 // head does the same work and the grid has no long tail.
+//
+// d = 64 runs the same kernel on 128-key tiles: a tile is again 16 KiB, the
+// copy plan and the waits are unchanged, and a step again holds 32 products
+// (its softmax covers twice the elements, which at d = 64 outweighs them).
+template <int D_>
 struct PPTile {
-  static constexpr int D = 128, BM = 256, BN = 64, WAVES = 8, THREADS = 512;
+  static constexpr int D = D_, BM = 256, BN = D_ == 128 ? 64 : 128, WAVES = 8, THREADS = 512;
   static constexpr int TILE = BN * D;                 // elements per K or V tile (16 KiB)
-  static constexpr int CPR = D / 8, RPI = 64 / CPR;   // 16 chunks per row, 4 rows per 1 KiB copy
+  static constexpr int CPR = D / 8, RPI = 64 / CPR;   // 16-byte chunks per row, rows per 1 KiB copy
   static constexpr int COPIES = BN / RPI / WAVES;     // 1 KiB copies per wave per tile (= 2)
 };
 
-template <bool CAUSAL, int MODE, int NBUF, bool PAIR>
+// Chunk swizzle of the V tiles, which are only read transposed: a half wave
+// reads 4 consecutive rows (from a multiple of 4) x 4 consecutive chunks.  At
+// d = 128 (256-byte rows) XOR-ing the chunk with 4*(r % 4) spreads them over
+// all 64 banks; at d = 64 (128-byte rows) rows r and r+2 share banks, and
+// XOR-ing with 4*((r/2) % 2) separates them.  Neither depends on bits above
+// the second, so moving 8 or 16 rows on leaves the swizzle unchanged.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  if constexpr (D == 128) return swz_v128(r);
+  else return 4 * ((r >> 1) & 1);
+}
+
+template <int D, bool CAUSAL, int MODE, int NBUF, bool PAIR>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_pp_kernel(FwdParams p) {
-  using T = PPTile;
-  constexpr int D = T::D, BM = T::BM, BN = T::BN;
+  using T = PPTile<D>;
+  constexpr int BM = T::BM, BN = T::BN;
+  constexpr int ST = D / 16, DB = D / 32, NS = BN / 16;  // k-steps, d-blocks, 16-key slices
   static_assert(NBUF == 3 || NBUF == 4, "ring depth");
   constexpr int KAHEAD = NBUF - 1, VAHEAD = NBUF - 2;  // tiles copied ahead of the one being used
   // buffers 0..NBUF-1: K tiles, NBUF..2*NBUF-1: V tiles; tile t lives in buffer t % NBUF.
@@ -415,7 +441,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int v_off[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)  // V region starts at buffer NBUF
-      v_off[db] = NBUF * T::TILE + tr_r * D + (((4 * db + tr_cc) ^ swz_v128(tr_r)) * 8) + tr_in;
+      v_off[db] = NBUF * T::TILE + tr_r * D + (((4 * db + tr_cc) ^ vswz<D>(tr_r)) * 8) + tr_in;
     // Fragment reads address lds0 + (per-step address register) + (a
     // compile-time offset): the step adds its buffer's base to the lane offsets
     // once, so one loop body serves every buffer.  The empty asm hides the lane
@@ -428,19 +454,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int db = 0; db < D / 32; ++db) asm volatile("" : "+v"(v_off[db]));
     const uint16_t* lds0 = kv_lds[0];
 
-    // Copy plan: wave w moves the 1 KiB copies c = 2w, 2w+1 (rows 4c .. 4c+3) of
-    // each K and V tile; lane l brings row 4c + l/16, source chunk
-    // (l % 16) ^ swizzle(row), to LDS position l % 16 (K: swz, V: swz_v128).
+    // Copy plan: wave w moves the 1 KiB copies c = 2w, 2w+1 (rows RPI*c ..
+    // RPI*c + RPI-1) of each K and V tile; lane l brings row RPI*c + l/CPR,
+    // source chunk (l % CPR) ^ swizzle(row), to LDS position l % CPR (K: swz,
+    // V: vswz).
     // The lane offsets of a full tile's copies are the same for every tile:
     // computed once here (bytes; the first copy's carries the +1 KiB bias of
     // copy16x2_to_lds).  Only the last tile of a sequence, where rows past the
     // length re-read the last valid row, adjusts them.
     static_assert(T::COPIES == 2, "copies are issued in pairs");
-    const int cp_r0 = (wave_u * T::COPIES) * T::RPI + (lane >> 4), cp_r1 = cp_r0 + T::RPI;
-    int cp_k0 = (cp_r0 * D + (((lane & 15) ^ swz<D>(cp_r0)) * 8)) * 2 + 1024;
-    int cp_k1 = (cp_r1 * D + (((lane & 15) ^ swz<D>(cp_r1)) * 8)) * 2;
-    int cp_v0 = (cp_r0 * D + (((lane & 15) ^ swz_v128(cp_r0)) * 8)) * 2 + 1024;
-    int cp_v1 = (cp_r1 * D + (((lane & 15) ^ swz_v128(cp_r1)) * 8)) * 2;
+    const int cp_r0 = (wave_u * T::COPIES) * T::RPI + lane / T::CPR, cp_r1 = cp_r0 + T::RPI;
+    const int cp_c = lane % T::CPR;
+    int cp_k0 = (cp_r0 * D + ((cp_c ^ swz<D>(cp_r0)) * 8)) * 2 + 1024;
+    int cp_k1 = (cp_r1 * D + ((cp_c ^ swz<D>(cp_r1)) * 8)) * 2;
+    int cp_v0 = (cp_r0 * D + ((cp_c ^ vswz<D>(cp_r0)) * 8)) * 2 + 1024;
+    int cp_v1 = (cp_r1 * D + ((cp_c ^ vswz<D>(cp_r1)) * 8)) * 2;
     asm volatile("" : "+v"(cp_k0), "+v"(cp_k1), "+v"(cp_v0), "+v"(cp_v1));
 
     float m = kNegInf, l = 0.f, lr = 0.f;
@@ -472,30 +500,52 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int ka[D / 16], va[D / 32];  // this step's K / V fragment offsets (elements)
     // Consecutive MFMAs always accumulate into different registers: a chain of
     // dependent MFMAs on one accumulator issues far below the matrix-core rate,
-    // two or more interleaved chains keep it busy.
-    //   S group g (0..3): k-steps 2g, 2g+1 for both key blocks, alternating
-    //   P.V group 4+i:    key slice i (16 keys) for all four d-blocks
+    // two or more interleaved chains keep it busy.  Four groups of four
+    // products for S, four for P.V:
+    //   S group g (0..3):  key blocks 2*kp, 2*kp+1 (alternating) at k-steps
+    //                      2*sp, 2*sp+1, with kp = g / (ST/2), sp = g % (ST/2)
+    //   P.V group 4+i:     16-key slices NS/4*i .. (all d-blocks, alternating)
+    auto s_item = [](int g, int i, int& kb, int& st) {
+      kb = 2 * (g / (ST / 2)) + (i & 1);
+      st = 2 * (g % (ST / 2)) + (i >> 1);
+    };
+    auto pv_item = [](int g, int i, int& sl, int& db) {
+      sl = (NS / 4) * (g - 4) + i / DB;
+      db = i % DB;
+    };
     auto load_group = [&](int g, bf16x8* f) {
       if (g < 4) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = *(const bf16x8*)(lds0 + ka[2 * g + (i >> 1)] + (i & 1) * 32 * D);
+        for (int i = 0; i < 4; ++i) {
+          int kb, st;
+          s_item(g, i, kb, st);
+          f[i] = *(const bf16x8*)(lds0 + ka[st] + kb * 32 * D);
+        }
       } else {
-        const int c = (((g - 4) >> 1) * 32 + 16 * ((g - 4) & 1)) * D;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          f[db] = join_bf16x8(lds_read_tr16(lds0 + va[db] + c), lds_read_tr16(lds0 + va[db] + c + 8 * D));
+        for (int i = 0; i < 4; ++i) {
+          int sl, db;
+          pv_item(g, i, sl, db);
+          const int c = 16 * sl * D;
+          f[i] = join_bf16x8(lds_read_tr16(lds0 + va[db] + c), lds_read_tr16(lds0 + va[db] + c + 8 * D));
+        }
       }
     };
     auto mfma_group = [&](int g, const bf16x8* f) {
       if (g < 4) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int kb = i & 1, st = 2 * g + (i >> 1);
+          int kb, st;
+          s_item(g, i, kb, st);
           s[kb] = mfma32x32x16(f[i], qf[st], st == 0 ? f32x16{} : s[kb]);
         }
       } else {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32x32x16(f[db], pf[g - 4], oacc[db]);
+        for (int i = 0; i < 4; ++i) {
+          int sl, db;
+          pv_item(g, i, sl, db);
+          oacc[db] = mfma32x32x16(f[i], pf[sl], oacc[db]);
+        }
       }
     };
     // The pipeline alternates P.V groups (G4..G7) and S groups (G0..G3): the
@@ -543,13 +593,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int k0 = j * BN;
       const bool need_mask = (k0 + BN > kv_len) || (CAUSAL && k0 + BN - 1 > w_first + diag);
       if (need_mask) {
-        // key k0 + 4*hi + c(kb, r) is visible iff c < rel
+        // key k0 + 4*hi + c(kb, r) is visible iff c < rel.  The sign of
+        // c - rel selects the score or -inf bit for bit.  (The element is
+        // copied to a scalar first: this compiler's __builtin_bit_cast of a
+        // vector element reads element 0 whatever the index.)
         const int rel = (CAUSAL ? min(kv_len, qrow + diag + 1) : kv_len) - k0 - 4 * hi;
+        const int ninf = __builtin_bit_cast(int, kNegInf);
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= rel) s[kb][r] = kNegInf;
+          for (int r = 0; r < 16; ++r) {
+            const int keep = (kb * 32 + 8 * (r >> 2) + (r & 3) - rel) >> 31;  // all ones iff visible
+            const float e = s[kb][r];
+            s[kb][r] = __builtin_bit_cast(float, (__builtin_bit_cast(int, e) & keep) | (ninf & ~keep));
+          }
       }
       // Row max, exponentials and the two row sums, with the reductions split
       // into four independent partial chains (short dependency chains keep the
@@ -590,7 +647,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           float t[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) t[e] = s[kb][8 * mm + e];
-          pf[kb * 2 + mm] = pack_bf16x8_sum(t, lrp[kb * 2 + mm]);
+          pf[kb * 2 + mm] = pack_bf16x8_sum(t, lrp[(kb * 2 + mm) & 3]);
         }
       lr += (lrp[0] + lrp[1]) + (lrp[2] + lrp[3]);
     };
@@ -713,13 +770,14 @@ static FwdParams make_params(const AttnArgs& a, int bm) {
   return p;
 }
 
-template <bool CAUSAL, int MODE, int NBUF = 3, bool PAIR = false>
+template <int D, bool CAUSAL, int MODE, int NBUF = 3, bool PAIR = false>
 static hipError_t launch_fwd_bf16_pp(const AttnArgs& a) {
-  const FwdParams p = make_params(a, PPTile::BM);
+  using T = PPTile<D>;
+  const FwdParams p = make_params(a, T::BM);
   const long long slots = PAIR ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
   const long long grid = slots * a.B * a.Hq;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_pp_kernel<CAUSAL, MODE, NBUF, PAIR>), dim3((unsigned)grid), dim3(PPTile::THREADS), 0,
+  hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, CAUSAL, MODE, NBUF, PAIR>), dim3((unsigned)grid), dim3(T::THREADS), 0,
                      a.stream, p);
   return hipGetLastError();
 }
@@ -735,10 +793,30 @@ static hipError_t launch_fwd_bf16_t(const AttnArgs& a) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (queried once per device).
+static int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int MODE>
 static hipError_t launch_mode(const AttnArgs& a) {
-  if (a.d == 128) return a.causal ? launch_fwd_bf16_pp<true, MODE>(a) : launch_fwd_bf16_pp<false, MODE>(a);
-  return a.causal ? launch_fwd_bf16_t<64, true, MODE>(a) : launch_fwd_bf16_t<64, false, MODE>(a);
+  if (a.d == 128) return a.causal ? launch_fwd_bf16_pp<128, true, MODE>(a) : launch_fwd_bf16_pp<128, false, MODE>(a);
+  if (!a.causal) return launch_fwd_bf16_pp<64, false, MODE>(a);
+  // d = 64 under a causal mask: the work of a query tile grows with its index,
+  // and a grid of fewer than two 256-row work-groups per CU runs as long as its
+  // heaviest tile while the CUs that drew light ones idle.  There the 128-row
+  // kernel (several work-groups per CU, half the tile) balances better.
+  const long long pp_grid = (long long)((a.Nq + PPTile<64>::BM - 1) / PPTile<64>::BM) * a.B * a.Hq;
+  if (pp_grid < 2LL * cu_count()) return launch_fwd_bf16_t<64, true, MODE>(a);
+  return launch_fwd_bf16_pp<64, true, MODE>(a);
 }
 
 hipError_t launch_fwd_bf16(const AttnArgs& a) {

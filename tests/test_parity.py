@@ -26,6 +26,20 @@ def test_cfg2_bf16_full(causal):
     check_fwd(q, k, v, causal=causal, what=f"cfg2 causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_cfg2_shape_on_a_large_grid(causal):
+    """d = 64 with enough heads that a causal grid has two 256-row work-groups
+    per CU (the ping-pong kernel; config 2 itself, causal, takes the 128-row
+    kernel): same seeds and distribution as config 2, 64 heads, sampled heads
+    compared in full, plus a padded variant with ragged lengths."""
+    q, k, v, _ = inputs.make_inputs(2, Hq=64, Hkv=64)
+    assert q.shape == (2, 64, 2048, 64)
+    heads = [(0, 0), (0, 31), (1, 5), (1, 63)]
+    check_fwd(q, k, v, causal=causal, heads=heads, what=f"cfg2 shape, 64 heads, causal={causal}")
+    lens = torch.tensor([2048 - 77, 1001], dtype=torch.int32)
+    check_fwd(q, k, v, causal=causal, lens=lens, heads=heads, what=f"cfg2 shape, 64 heads, padded, causal={causal}")
+
+
 def test_cfg3_reduced_full_compare():
     # same seeds and distribution, fewer heads and a ragged length
     q, k, v, _ = inputs.make_inputs(3, Hq=2, Hkv=2, Nq=1000, Nk=1000)

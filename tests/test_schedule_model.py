@@ -1,7 +1,8 @@
 """CPU models of the prefill kernels' LDS protocol and copy addressing.
 
-The d=128 prefill kernel (fwd_bf16_pp_kernel) runs two groups of four waves
-one barrier apart; K and V tiles rotate through rings of LDS buffers filled by
+The prefill kernel (fwd_bf16_pp_kernel, d=128 on 64-key tiles and d=64 on
+128-key tiles, the same 16 KiB per tile and the same copies and waits) runs
+two groups of four waves one barrier apart; K and V tiles rotate through rings of LDS buffers filled by
 asynchronous global->LDS copies that each wave issues for its own rows, waits
 on with s_waitcnt vmcnt(N), and publishes with s_barrier.  A tile may only be
 read once every wave's copy into its buffer has been waited on before a
@@ -16,7 +17,10 @@ schedules (copies waited too late; a work-group with no visible tile copying
 tile -1) must fail.
 
 The address models below mirror each copy routine's index arithmetic and
-check that every global row it touches lies inside its sequence.
+check that every global row it touches lies inside its sequence, that the
+LDS swizzles spread every fragment read over all banks, and that every K and
+V fragment read of the prefill kernel finds in LDS the (row, chunk) its copy
+put there.
 """
 import pytest
 
@@ -451,8 +455,9 @@ def test_bwd_schedule_variants_race(bad):
 # Copy addressing: every global row a copy reads lies in [0, kv_len)
 def pp_copy_rows(t, n_kt, kv_len, BN=64, waves=8, rows_per_copy=4):
     """Rows read by the ping-pong kernel's copy_tile for tile t: the tile is
-    clamped to n_kt - 1; each wave copies rows 4c .. 4c+3 for its two copies c,
-    and rows past the length re-read the last valid row."""
+    clamped to n_kt - 1; each wave copies rows RPI*c .. RPI*c + RPI-1 for its
+    two copies c, and rows past the length re-read the last valid row.
+    (d = 128: 64-key tiles, 4 rows per copy; d = 64: 128-key tiles, 8 rows.)"""
     t = min(t, n_kt - 1)
     k0 = t * BN
     rows = []
@@ -474,18 +479,25 @@ def n_tiles(kv_len, causal, q0, bm, nq, diag, BN=64):
     return (kend + BN - 1) // BN if kend > 0 else 0
 
 
+PP_TILES = {128: (64, 4), 64: (128, 8)}  # d -> (keys per tile, rows per 1 KiB copy)
+
+
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("nq,nk,kv_len,causal", [
     (1, 1, 1, False), (64, 64, 64, True), (65, 65, 65, True), (300, 300, 300, True), (300, 300, 129, True),
     (200, 5, 5, False), (5, 200, 200, True), (256, 256, 0, True), (300, 100, 100, True), (513, 513, 300, False),
+    (77, 300, 300, True),
 ])
-def test_pp_copies_stay_inside_the_sequence(nq, nk, kv_len, causal):
+def test_pp_copies_stay_inside_the_sequence(nq, nk, kv_len, causal, d):
+    BN, rpc = PP_TILES[d]
     diag = nk - nq
     for q0 in range(0, nq, 256):
-        nkt = n_tiles(kv_len, causal, q0, 256, nq, diag)
+        nkt = n_tiles(kv_len, causal, q0, 256, nq, diag, BN)
         if nkt == 0:
             continue  # the kernel issues no copy at all (guarded)
         for t in range(0, nkt + 4):
-            rows = pp_copy_rows(t, nkt, kv_len)
+            rows = pp_copy_rows(t, nkt, kv_len, BN, rows_per_copy=rpc)
+            assert len(rows) == BN
             assert min(rows) >= 0 and max(rows) < kv_len, (q0, t, min(rows), max(rows))
 
 
@@ -509,7 +521,11 @@ def swz_v128(r):
     return 4 * (r & 3)
 
 
-@pytest.mark.parametrize("D,swz", [(128, swz128), (64, swz64), (128, swz_v128)])
+def swz_v64(r):
+    return 4 * ((r >> 1) & 1)
+
+
+@pytest.mark.parametrize("D,swz", [(128, swz128), (64, swz64), (128, swz_v128), (64, swz_v64)])
 def test_swizzles_are_bijections_per_row(D, swz):
     cpr = D // 8
     for r in range(64):
@@ -540,11 +556,12 @@ def test_k_fragment_reads_cover_all_banks(D, swz):
             assert sorted(_banks(addrs)) == list(range(64)), (st, quarter)
 
 
-def test_v_transposed_reads_cover_all_banks():
-    """ds_read_b64_tr_b16 of V (d=128, swz_v128): in each half wave, 4 rows x 4
-    chunks (8 bytes per lane) cover the 64 banks once per 32 lanes."""
-    D = 128
-    for db in range(4):
+@pytest.mark.parametrize("D,vswz", [(128, swz_v128), (64, swz_v64)])
+def test_v_transposed_reads_cover_all_banks(D, vswz):
+    """ds_read_b64_tr_b16 of V: in each half wave, 4 rows x 4 chunks (8 bytes
+    per lane) cover the 64 banks once per 32 lanes, for every d-block and
+    both reads of a pair (8 rows apart)."""
+    for db in range(D // 32):
         for u in range(2):
             for half in range(2):
                 addrs = []
@@ -554,9 +571,82 @@ def test_v_transposed_reads_cover_all_banks():
                     tr_cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)
                     tr_in = 4 * (lane & 1)
                     r = 8 * u + tr_r
-                    elem = r * D + (((4 * db + tr_cc) ^ swz_v128(r)) * 8) + tr_in
+                    elem = r * D + (((4 * db + tr_cc) ^ vswz(r)) * 8) + tr_in
                     addrs.append(elem * 2)
                 banks = []
                 for a in addrs:
                     banks.extend(((a // 4) + i) % 64 for i in range(2))
-                assert sorted(banks) == list(range(64)), (db, u, half)
+                assert sorted(banks) == list(range(64)), (D, db, u, half)
+
+
+# ---------------------------------------------------------------------------
+# Copy -> fragment-read agreement in the ping-pong kernel, for both head
+# dimensions: the LDS tile the sixteen 1 KiB copies build, and the (row,
+# chunk) every K and V fragment read then finds there.
+def pp_lds_tile(D, is_v):
+    """Replays copy_tile's LDS writes: {LDS element offset of a 16-byte chunk:
+    (tile row, source chunk)}.  Wave w's copies c = 2w, 2w+1 write LDS bytes
+    [1024 c, 1024 c + 1024); lane l writes 16 bytes at 1024 c + 16 l, read
+    from row RPI*c + l // CPR, chunk (l % CPR) ^ swizzle(row)."""
+    BN, rpi = PP_TILES[D]
+    cpr = D // 8
+    swz = (swz_v128 if D == 128 else swz_v64) if is_v else (swz128 if D == 128 else swz64)
+    tile = {}
+    for c in range(BN // rpi):
+        for lane in range(64):
+            row = rpi * c + lane // cpr
+            elem = (1024 * c + 16 * lane) // 2
+            assert elem not in tile
+            tile[elem] = (row, (lane % cpr) ^ swz(row))
+    assert len(tile) == BN * cpr
+    return tile
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_pp_k_reads_find_their_rows(D):
+    BN, _ = PP_TILES[D]
+    swz = swz128 if D == 128 else swz64
+    tile = pp_lds_tile(D, False)
+    for kb in range(BN // 32):
+        for st in range(D // 16):
+            for lane in range(64):
+                li, hi = lane & 31, lane >> 5
+                off = li * D + (((2 * st + hi) ^ swz(li)) * 8) + kb * 32 * D
+                assert tile[off] == (32 * kb + li, 2 * st + hi), (D, kb, st, lane)
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_pp_v_reads_find_their_rows(D):
+    BN, _ = PP_TILES[D]
+    vswz = swz_v128 if D == 128 else swz_v64
+    tile = pp_lds_tile(D, True)
+    for sl in range(BN // 16):
+        for db in range(D // 32):
+            for u in range(2):
+                for lane in range(64):
+                    hi = lane >> 5
+                    tr_r = 4 * hi + ((lane & 15) >> 2)
+                    tr_cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)
+                    tr_in = 4 * (lane & 1)
+                    off = tr_r * D + (((4 * db + tr_cc) ^ vswz(tr_r)) * 8) + tr_in + 16 * sl * D + 8 * u * D
+                    base = off - tr_in  # the 16-byte chunk the 8 bytes lie in
+                    assert tile[base] == (16 * sl + 8 * u + tr_r, 4 * db + tr_cc), (D, sl, db, u, lane)
+
+
+def test_pp_v_read_with_a_row_dependent_swizzle_misses():
+    # planted mistake: swz64 (which depends on row bit 3) for d = 64 V tiles
+    # breaks the constant per-lane offsets of the second read of a pair
+    D = 64
+    tile = {}
+    for c in range(16):
+        for lane in range(64):
+            row = 8 * c + lane // 8
+            tile[(1024 * c + 16 * lane) // 2] = (row, (lane % 8) ^ swz64(row))
+    bad = 0
+    for lane in range(64):
+        hi = lane >> 5
+        tr_r = 4 * hi + ((lane & 15) >> 2)
+        tr_cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)
+        off = tr_r * D + ((tr_cc ^ swz64(tr_r)) * 8) + 8 * D
+        bad += tile[off] != (8 + tr_r, tr_cc)
+    assert bad > 0
