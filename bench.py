@@ -92,12 +92,12 @@ def load_traffic(kernel):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
-def load_mfma_busy(kernel):
-    """Fraction of SIMD cycles the matrix cores were busy during the kernel,
-    from the committed counter runs on the current sources; else None."""
+def load_util(kernel):
+    """Matrix-core busy fraction of SIMD cycles and the sustained clock during
+    the kernel, from the committed counter runs on the current sources; else
+    None."""
     rec = _counters()
-    k = None if rec is None else rec.get("utilisation", {}).get(kernel)
-    return None if k is None else k.get("mfma_busy_frac")
+    return None if rec is None else rec.get("utilisation", {}).get(kernel)
 
 
 def stats_ms(ms):
@@ -176,7 +176,7 @@ def time_calls(call, n, stream):
     return [e0.elapsed_time(e1) for e0, e1 in ev]
 
 
-def mfma_leg(ms, flop, kernel, workload, ceiling=None, busy=None, traffic=None, peak=PEAK_BF16_TFLOPS):
+def mfma_leg(ms, flop, kernel, workload, ceiling=None, util=None, traffic=None, peak=PEAK_BF16_TFLOPS):
     """Record of a matrix-core-bound leg from its per-launch durations."""
     st = stats_ms(ms)
     tf = flop / (st["mean_ms"] * 1e-3) / 1e12
@@ -186,8 +186,9 @@ def mfma_leg(ms, flop, kernel, workload, ceiling=None, busy=None, traffic=None, 
     if ceiling:
         roof["measured_ceiling"] = round(ceiling, 1)
         roof["frac_of_measured_ceiling"] = round(tf / ceiling, 4)
-    if busy is not None:
-        roof["counter_mfma_busy_frac"] = busy
+    if util:
+        roof["counter_mfma_busy_frac"] = util.get("mfma_busy_frac")
+        roof["counter_clock_ghz"] = util.get("clock_ghz")
     return {"value": round(tf, 2), "unit": "TFLOP/s", "workload": workload, "flop_per_call": flop, **st,
             "roofline": roof}
 
@@ -407,7 +408,7 @@ def main():
 
     f_fwd = prefill_flops(c3["B"], c3["Hq"], c3["Nq"], c3["Nk"], c3["d"], True)
     main = mfma_leg(fwd_ms, f_fwd, "fwd_bf16_pp_kernel<causal>", "prefill fwd B=1 H=32 N=8192 d=128 causal bf16",
-                    mfma_ceiling, load_mfma_busy("fwd_bf16_pp_kernel"), load_traffic("fwd_bf16_pp_kernel"))
+                    mfma_ceiling, load_util("fwd_bf16_pp_kernel"), load_traffic("fwd_bf16_pp_kernel"))
     fwd_tflops = main["value"]
     dbytes = decode_bytes(B5, Hq5, Hkv5, Nk5, d5)
     dst = stats_ms(dec_ms)
@@ -423,6 +424,7 @@ def main():
         q2, k2, v2 = [t.to(dev) for t in inputs.make_inputs(2)[:3]]
         o2, l2 = torch.empty_like(q2), torch.empty(q2.shape[:3], dtype=torch.float32, device=dev)
         side["prefill_d64"] = {}
+        d64_key = {True: "fwd_bf16_kernel_d64", False: "fwd_bf16_pp_kernel_d64"}
         for causal in (True, False):
             call = lambda: fa.fa_fwd(q2, k2, v2, causal=causal, out=o2, lse=l2)  # noqa: E731
             warm(call)
@@ -432,7 +434,8 @@ def main():
             side["prefill_d64"][name] = mfma_leg(
                 ms, fl, "fwd_bf16_kernel<64,causal> (256 ping-pong work-groups would not fill two per CU)"
                 if causal else "fwd_bf16_pp_kernel<64,non-causal>",
-                f"prefill fwd B=2 H=16 N=2048 d=64 {'causal' if causal else 'non-causal'} bf16", mfma_ceiling)
+                f"prefill fwd B=2 H=16 N=2048 d=64 {'causal' if causal else 'non-causal'} bf16", mfma_ceiling,
+                load_util(d64_key[causal]), load_traffic(d64_key[causal]))
             log(f"d64 {name}: {side['prefill_d64'][name]['value']} TFLOP/s")
         del q2, k2, v2, o2, l2
 
@@ -448,7 +451,7 @@ def main():
         side["prefill_gqa_padded"] = mfma_leg(
             ms, fl, "fwd_bf16_pp_kernel<causal,padded>",
             f"prefill fwd B=4 Hq=32 Hkv=8 N=4096 d=128 causal bf16, kv lengths {L4}", mfma_ceiling,
-            load_mfma_busy("fwd_bf16_pp_kernel_padded"), load_traffic("fwd_bf16_pp_kernel_padded"))
+            load_util("fwd_bf16_pp_kernel_padded"), load_traffic("fwd_bf16_pp_kernel_padded"))
         log(f"gqa padded: {side['prefill_gqa_padded']['value']} TFLOP/s")
         del q4, k4, v4, o4, l4
 
@@ -463,7 +466,7 @@ def main():
         f_bwd = 2.5 * f_fwd
         bwd = mfma_leg(ms, f_bwd, "bwd kernels (fa_bwd)",
                        "backward of prefill B=1 H=32 N=8192 d=128 causal bf16 (dQ, dK, dV)", mfma_ceiling,
-                       None, load_traffic("fa_bwd"))
+                       load_util("fa_bwd"), load_traffic("fa_bwd"))
         bwd["flop_count"] = ("5 products of 2*d FLOP per visible (query, key) pair: S recomputed, dP, dV, dK, dQ "
                              "(2.5x the forward)")
         side["backward"] = bwd
@@ -507,7 +510,8 @@ def main():
             varlen[name] = mfma_leg(
                 ms, fl, "fwd_bf16_pp_kernel<causal,packed>",
                 f"fa_fwd_varlen Hq=32 Hkv=8 d=128 causal bf16, key lengths {lens}, query lengths {lq}",
-                mfma_ceiling, None, load_traffic("fwd_bf16_pp_kernel_packed") if name == "packed" else None)
+                mfma_ceiling, load_util("fwd_bf16_pp_kernel_packed") if name == "packed" else None,
+                load_traffic("fwd_bf16_pp_kernel_packed") if name == "packed" else None)
             log(f"varlen {name}: {varlen[name]['value']} TFLOP/s")
             del qv, kv_, vv, ov, lv
         side["prefill_varlen"] = varlen
@@ -520,7 +524,7 @@ def main():
         ms = time_calls(call, n_side, stream)
         fp8 = mfma_leg(ms, f_fwd, "fwd_fp8_pp_kernel<e4m3,causal>",
                        "fa_fwd_fp8 E4M3 B=1 H=32 N=8192 d=128 causal (per-tensor descales), bf16 output",
-                       None, None, load_traffic("fwd_fp8_pp_kernel"), peak=PEAK_FP8_TFLOPS)
+                       None, load_util("fwd_fp8_pp_kernel"), load_traffic("fwd_fp8_pp_kernel"), peak=PEAK_FP8_TFLOPS)
         fp8["roofline"]["peak_note"] = "dense FP8 matrix-core peak; Q.K^T runs on FP8, P.V on bf16 matrix cores"
         fp8["roofline"]["mixed_peak"] = round(PEAK_FP8_BF16_MIX_TFLOPS, 1)
         fp8["roofline"]["frac_of_mixed_peak"] = round(fp8["value"] / PEAK_FP8_BF16_MIX_TFLOPS, 4)

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int wave = tid >> 6, lane = tid & 63, li = lane & 31, hi = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int bh_count = p.B * p.Hq;
-  const int bh = blockIdx.x % bh_count;
+  const int bh = xcd_grouped_head((int)(blockIdx.x % bh_count), p.B, p.Hq, p.Hkv);  // a KV head's heads on one XCD
   const int qt = p.n_tiles - 1 - (int)(blockIdx.x / bh_count);  // heaviest (causal) first
   const int b = bh / p.Hq, hq = bh - b * p.Hq;
   const int hk = hq / (p.Hq / p.Hkv);

@@ -154,6 +154,22 @@ __device__ __forceinline__ int swz(int r) {
 // banks, and rows 8 apart share one swizzle (their offset is an immediate).
 __device__ __forceinline__ int swz_v128(int r) { return 4 * (r & 3); }
 
+// (batch, query head) of slot j of a query-tile slot's B*Hq work-groups.
+// Work-groups are dispatched to the 8 XCDs round-robin (XCD = block index mod
+// 8, and B*Hq is then a multiple of 8), each XCD with its own L2.  The g
+// query heads of a KV head read the same K/V tiles: when the (batch, KV head)
+// groups divide evenly over the XCDs, slot j = 8c + x goes to group
+// x + 8*(c / g), head c % g of it, so a group's heads all run on XCD x and
+// its K/V is fetched into one L2 instead of g.  Otherwise heads stay in order.
+__device__ __forceinline__ int xcd_grouped_head(int j, int B, int Hq, int Hkv) {
+  const int g = Hq / Hkv;
+  if (g == 1 || (B * Hkv) % 8 != 0) return j;
+  const int x = j & 7, c = j >> 3;
+  const int group = x + 8 * (c / g);
+  const int b = group / Hkv, hk = group - b * Hkv;
+  return b * Hq + hk * g + (c - (c / g) * g);
+}
+
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 // max / sum of x over the lane pair (l, l ^ 32) with one v_permlane32_swap:

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool lead = wave_u < 4;  // group 0 leads, group 1 lags one phase
 
   const int bh_count = p.B * p.Hq;
-  const int bh = blockIdx.x % bh_count;
+  const int bh = xcd_grouped_head((int)(blockIdx.x % bh_count), p.B, p.Hq, p.Hkv);
   const int qt = p.n_qtiles - 1 - (int)(blockIdx.x / bh_count);
   const int b = bh / p.Hq, hq = bh - b * p.Hq;
   const int hk = hq / (p.Hq / p.Hkv);

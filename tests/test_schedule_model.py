@@ -650,3 +650,35 @@ def test_pp_v_read_with_a_row_dependent_swizzle_misses():
         off = tr_r * D + ((tr_cc ^ swz64(tr_r)) * 8) + 8 * D
         bad += tile[off] != (8 + tr_r, tr_cc)
     assert bad > 0
+
+
+# ---------------------------------------------------------------------------
+# Work-group -> (batch, query head) in the forward and dQ kernels: a
+# permutation of each query-tile slot's B*Hq work-groups that puts the g query
+# heads of a KV head on one XCD (round-robin dispatch: XCD = block index mod 8)
+def xcd_grouped_head(j, B, Hq, Hkv):
+    g = Hq // Hkv
+    if g == 1 or (B * Hkv) % 8 != 0:
+        return j
+    x, c = j & 7, j >> 3
+    group = x + 8 * (c // g)
+    b, hk = group // Hkv, group % Hkv
+    return b * Hq + hk * g + c % g
+
+
+@pytest.mark.parametrize("B,Hq,Hkv", [(4, 32, 8), (1, 32, 8), (2, 64, 8), (8, 8, 1), (1, 32, 32), (3, 32, 8),
+                                      (2, 16, 4), (1, 8, 2), (16, 64, 1)])
+def test_head_mapping_is_a_permutation_grouped_by_xcd(B, Hq, Hkv):
+    bh_count = B * Hq
+    for slot in range(3):
+        heads = []
+        for j in range(bh_count):
+            block = slot * bh_count + j
+            bh = xcd_grouped_head(block % bh_count, B, Hq, Hkv)
+            heads.append(bh)
+            g = Hq // Hkv
+            if g > 1 and (B * Hkv) % 8 == 0:
+                b, hq = divmod(bh, Hq)
+                kv_group = b * Hkv + hq // g
+                assert kv_group % 8 == block % 8, (B, Hq, Hkv, block)  # same XCD for a KV head's heads
+        assert sorted(heads) == list(range(bh_count))
