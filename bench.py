@@ -217,7 +217,7 @@ def ceilings(dev, stream, read_buf):
                     "what": f"fa_ceiling_mfma: {blocks} work-groups x 4 waves, {iters * 32} products per wave in 4 "
                             f"independent v_mfma_f32_32x32x16_bf16 chains, {what} (fastest launch)",
                     **stats_ms(ms)}
-    rblocks = 8 * cu
+    rblocks = 2 * cu
     ro = torch.empty(rblocks * 256, dtype=torch.int32, device=dev)
     nbytes = read_buf.numel() * read_buf.element_size()
     rd = lambda: lib.fa_ceiling_read(read_buf.data_ptr(), nbytes, ro.data_ptr(), rblocks, stream.cuda_stream)  # noqa: E731
@@ -226,8 +226,9 @@ def ceilings(dev, stream, read_buf):
     rst = stats_ms(rms)
     read_gbs = nbytes / (min(rms) * 1e-3) / 1e9
     res["hbm_read"] = {"value": round(read_gbs, 1), "unit": "GB/s", "frac_of_peak": round(read_gbs / PEAK_HBM_GBS, 4),
-                       "what": f"fa_ceiling_read: {nbytes} bytes read once, 16-byte nontemporal loads "
-                               "(fastest launch)", **rst}
+                       "what": f"fa_ceiling_read: {nbytes} bytes read once by {rblocks} work-groups, each a "
+                               "contiguous run with eight 16-byte nontemporal loads in flight per lane (fastest launch)",
+                       **rst}
     return res
 
 

@@ -7,8 +7,8 @@
 //    depends on the data: on random operands the chip holds a lower clock
 //    than on small constants (power), so both are measured.
 //  * ceiling_read_kernel: a streaming read of a large buffer with 16-byte
-//    nontemporal loads, four in flight per lane -- the HBM rate the decode can
-//    at best approach.
+//    nontemporal loads, each work-group on its own contiguous run with eight
+//    loads in flight per lane -- the HBM rate the decode can at best approach.
 //
 // These are measurement aids; no attention entry point uses them.
 #include "fa_ceilings.h"
@@ -58,19 +58,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   out[(size_t)blockIdx.x * 256 + tid] = s;
 }
 
+// Each work-group streams its own contiguous run of the buffer (a whole
+// multiple of 256 x 8 16-byte units), eight nontemporal loads in flight per
+// lane; the units past the last run are read grid-stride.
 __global__ __launch_bounds__(256) void ceiling_read_kernel(const u32x4* __restrict__ src, size_t n16,
                                                            unsigned* out) {
-  const size_t stride = (size_t)gridDim.x * 256;
-  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  constexpr int U = 8;
+  const size_t per = (n16 / gridDim.x) / (256 * U) * (256 * U);
+  const u32x4* p = src + (size_t)blockIdx.x * per + threadIdx.x;
   unsigned acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    u32x4 x[4];
+  for (size_t i = 0; i < per; i += 256 * U) {
+    u32x4 x[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) x[u] = __builtin_nontemporal_load(src + i + u * stride);
+    for (int u = 0; u < U; ++u) x[u] = __builtin_nontemporal_load(p + i + u * 256);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc ^= x[u][0] ^ x[u][1] ^ x[u][2] ^ x[u][3];
+    for (int u = 0; u < U; ++u) acc ^= x[u][0] ^ x[u][1] ^ x[u][2] ^ x[u][3];
   }
-  for (; i < n16; i += stride) {
+  for (size_t i = (size_t)gridDim.x * per + (size_t)blockIdx.x * 256 + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * 256) {
     const u32x4 x = __builtin_nontemporal_load(src + i);
     acc ^= x[0] ^ x[1] ^ x[2] ^ x[3];
   }

@@ -34,8 +34,10 @@ int fa_ceiling_mfma(const void* src, float* out, int blocks, int iters, void* st
 /*
  * fa_ceiling_read -- `blocks` work-groups of 256 threads read `bytes` bytes at
  * `src` (DEVICE, 16-byte aligned, bytes a multiple of 16) once with 16-byte
- * nontemporal loads, four in flight per lane.  out: DEVICE
- * unsigned[blocks * 256], written (an xor of what each thread read).
+ * nontemporal loads: each work-group streams its own contiguous run, eight
+ * loads in flight per lane (units past the last whole run are read
+ * grid-stride).  out: DEVICE unsigned[blocks * 256], written (an xor of what
+ * each thread read).
  */
 int fa_ceiling_read(const void* src, size_t bytes, unsigned* out, int blocks, void* stream);
 
