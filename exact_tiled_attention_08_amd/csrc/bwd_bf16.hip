@@ -94,7 +94,7 @@ template <int D, bool CAUSAL, bool PADDED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdParams p) {
   constexpr int BM = 128, BN = 32, TK = BN * D;
   constexpr int RPI = 64 / (D / 8), COPIES = BN / RPI / 4;  // 1 KiB copies per wave per K (or V) tile
-  __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[2][2][TK];  // [buffer][K, V]
+  __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[3][2][TK];  // [buffer][K, V]
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, li = lane & 31, hi = lane >> 5;
@@ -157,22 +157,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       copy_tile_rows<D>(vg, t * BN, kv_len, c, kv_lds[buf][1], lane);
     }
   };
-  if (n_kt > 0) {
-    issue(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-  for (int t = 0; t < n_kt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_kt) issue(t + 1, buf ^ 1);
+  // S^T = K Q^T and dP^T = V dO^T of the tile in buffer `buf`, fragments read
+  // one k-step ahead.
+  auto sdp = [&](int buf, f32x16& s, f32x16& dp) {
     const uint16_t* kl = kv_lds[buf][0];
     const uint16_t* vl = kv_lds[buf][1];
-    const int k0 = t * BN;
-
-    // Fragments are read one k-step (one d-block below) ahead; the
-    // scheduling barriers keep the compiler from hoisting every read.
-    f32x16 s = f32x16{}, dp = f32x16{};
+    s = f32x16{};
+    dp = f32x16{};
     bf16x8 fk[2], fv[2];
     fk[0] = *(const bf16x8*)(kl + tile_off<D>(li, hi));
     fv[0] = *(const bf16x8*)(vl + tile_off<D>(li, hi));
@@ -184,23 +175,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       s = mfma32x32x16(fk[st & 1], qf[st], s);
       dp = mfma32x32x16(fv[st & 1], dof[st], dp);
-      __builtin_amdgcn_sched_barrier(0);
     }
-    // lane l: query qrow; register r: key k0 + 8(r/4) + 4*hi + r%4.  Tiles
-    // whose keys are all valid and visible to every row of the wave skip the
-    // per-element mask (rows past Nq have LSE +inf, so their P is 0 anyway).
+  };
+
+  // Software pipeline over 32-key tiles in a ring of three LDS buffers:
+  // iteration t starts the copy of tile t+2, computes S and dP of tile t+1
+  // (matrix cores) beside the softmax of tile t (vector ALU), then dQ += K^T
+  // dS of tile t.  Tile t+1 was copied one iteration earlier and waited for
+  // before the barrier that ended it; buffer (t+2) % 3 last held tile t-1,
+  // whose last reads were retired before that barrier.  (tests/
+  // test_schedule_model.py replays this schedule.)
+  f32x16 s_cur = f32x16{}, dp_cur = f32x16{};
+  if (n_kt > 0) {
+    issue(0, 0);
+    if (n_kt > 1) issue(1, 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (n_kt > 0) sdp(0, s_cur, dp_cur);
+
+  int b_cur = 0;  // buffer of tile t
+  for (int t = 0; t < n_kt; ++t) {
+    const int b_nxt = b_cur == 2 ? 0 : b_cur + 1, b_far = b_nxt == 2 ? 0 : b_nxt + 1;
+    if (t + 2 < n_kt) issue(t + 2, b_far);
+    // S, dP of tile t+1 (after the last tile: finite data nothing uses).
+    f32x16 s_nxt, dp_nxt;
+    sdp(b_nxt, s_nxt, dp_nxt);
+
+    // lane l: query qrow; register r: key k0 + 8(r/4) + 4*hi + r%4.  The
+    // exponential runs for every element (rows past Nq have LSE +inf, keys
+    // past the length read finite rows); tiles that are not all valid and
+    // visible to every row of the wave then zero what is not, in a branch of
+    // their own so the common path stays one straight-line block.
+    const int k0 = t * BN;
     float ds[16];
-    if (k0 + BN <= kv_len && (!CAUSAL || k0 + BN - 1 <= q0 + wave_u * 32 + diag)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -lse2)) * (dp[r] - drow);
-    } else {
+    for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(__builtin_fmaf(s_cur[r], p.scale_log2, -lse2)) * (dp_cur[r] - drow);
+    if (!(k0 + BN <= kv_len && (!CAUSAL || k0 + BN - 1 <= q0 + wave_u * 32 + diag))) {
+      asm volatile("");
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + 8 * (r >> 2) + 4 * hi + (r & 3);
         bool vis = key < kv_len;
-        if (CAUSAL) vis = vis && key <= qrow + diag;
-        const float pr = vis ? fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -lse2)) : 0.f;
-        ds[r] = pr * (dp[r] - drow);
+        if (CAUSAL) vis = vis & (key <= qrow + diag);
+        ds[r] = vis ? ds[r] : 0.f;
       }
     }
     bf16x8 dsf[2];
@@ -209,17 +227,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // Key slice mm outermost: consecutive products accumulate into different
     // d-blocks (a product that waits for the previous one's accumulator
     // stalls the matrix core).
+    const uint16_t* kl = kv_lds[b_cur][0];
     constexpr int NF = 2 * (D / 32);
-    bf16x8 kt[2];
-    kt[0] = tr_fragment<D>(kl, 0, 0, lane);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int mm = f / (D / 32), db = f % (D / 32);
-      if (f + 1 < NF) kt[(f + 1) & 1] = tr_fragment<D>(kl, 16 * ((f + 1) / (D / 32)), (f + 1) % (D / 32), lane);
-      dq_acc[db] = mfma32x32x16(kt[f & 1], dsf[mm], dq_acc[db]);
-      __builtin_amdgcn_sched_barrier(0);
+      dq_acc[db] = mfma32x32x16(tr_fragment<D>(kl, 16 * mm, db, lane), dsf[mm], dq_acc[db]);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next tile's copies
+    s_cur = s_nxt;
+    dp_cur = dp_nxt;
+    b_cur = b_nxt;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile t+2's copies
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 

@@ -437,6 +437,76 @@ def replay_bwd(n_it, nbuf=2, end_wait=0, ahead=1):
     return writes, reads
 
 
+def replay_dq(n_kt, nbuf=3, ahead=2, prologue_wait=0, end_wait=0):
+    """The dQ kernel's pipeline: the prologue copies tiles 0 .. ahead-1 and
+    waits (vmcnt(prologue_wait)); iteration t copies tile t+ahead into buffer
+    (t+ahead) % nbuf, reads tile t+1 (S and dP) and tile t (K^T for dQ),
+    waits (vmcnt(end_wait)) and passes a barrier.  Each wave copies 8 of the
+    32 rows of every K and V tile."""
+    n_waves = 4
+    waves = [Wave(w, 0) for w in range(n_waves)]
+    rows = {w: frozenset(range(8 * w, 8 * w + 8)) for w in range(n_waves)}
+    writes, reads = [], []
+    for w in waves:
+        w.landed, w.issued = [], []
+
+        def write(buf, tile, owners, w=w):
+            c = {"issuer": w.wid, "owners": owners, "buf": buf, "tile": tile, "issue": w.epoch, "publish": None,
+                 "idx": len(writes)}
+            writes.append(c)
+            w.vm.extend([c, c])
+            w.issued.append(c)
+
+        def wait(n, w=w):
+            w.vm = w.vm[max(0, len(w.vm) - n):]
+            pending = {id(c) for c in w.vm}
+            for c in w.issued:
+                if c["publish"] is None and id(c) not in pending and c not in w.landed:
+                    w.landed.append(c)
+
+        def barrier(w=w):
+            for c in w.landed:
+                if c["publish"] is None:
+                    c["publish"] = w.epoch + 1
+            w.landed = []
+            w.epoch += 1
+
+        def read(buf, tile, w=w):
+            reads.append({"wave": w.wid, "buf": buf, "tile": tile, "epoch": w.epoch})
+
+        for t in range(min(ahead, n_kt)):
+            write(("KV", t % nbuf), ("tile", t), rows[w.wid])
+        if n_kt > 0:
+            wait(prologue_wait)
+        barrier()
+        if n_kt > 0:
+            read(("KV", 0), ("tile", 0))
+        for t in range(n_kt):
+            if t + ahead < n_kt:
+                write(("KV", (t + ahead) % nbuf), ("tile", t + ahead), rows[w.wid])
+            if t + 1 < n_kt:
+                read(("KV", (t + 1) % nbuf), ("tile", t + 1))
+            read(("KV", t % nbuf), ("tile", t))
+            wait(end_wait)
+            barrier()
+    return writes, reads
+
+
+@pytest.mark.parametrize("n_kt", [1, 2, 3, 4, 5, 9, 20])
+def test_dq_pipeline_is_race_free(n_kt):
+    writes, reads = replay_dq(n_kt)
+    assert check_schedule(writes, reads) == []
+
+
+@pytest.mark.parametrize("bad", [dict(prologue_wait=2), dict(end_wait=2), dict(nbuf=2), dict(ahead=3)])
+def test_dq_pipeline_variants_race(bad):
+    # a prologue that waits only for tile 0 (tile 1 is read in iteration 0), a
+    # step-end wait that lets the next tile's copies run on, two buffers, or
+    # copies three tiles ahead into a three-buffer ring all break it
+    writes, reads = replay_dq(6, **bad)
+    assert check_schedule(writes, reads) != []
+
+
 @pytest.mark.parametrize("n_it", [1, 2, 3, 4, 7, 20])
 def test_bwd_schedule_is_race_free(n_it):
     writes, reads = replay_bwd(n_it)
