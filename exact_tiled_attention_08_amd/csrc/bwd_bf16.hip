@@ -244,14 +244,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (row_ok) {
     uint16_t* op = p.dq + (qrow_base + qrow) * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint2 w;
-        w.x = pack_bf16x2(dq_acc[db][4 * g] * p.scale, dq_acc[db][4 * g + 1] * p.scale);
-        w.y = pack_bf16x2(dq_acc[db][4 * g + 2] * p.scale, dq_acc[db][4 * g + 3] * p.scale);
-        *(uint2*)(op + db * 32 + 8 * g + 4 * hi) = w;
-      }
+    for (int db = 0; db < D / 32; ++db) store_row_bf16x32(op + db * 32, dq_acc[db], p.scale, hi);
   }
 }
 
@@ -461,17 +454,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     uint16_t* dvp = p.dv + (kv_base + key) * D;
     uint16_t* dkp = p.dk + (kv_base + key) * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        uint2 w;
-        w.x = pack_bf16x2(acc_dv[db][4 * g4], acc_dv[db][4 * g4 + 1]);
-        w.y = pack_bf16x2(acc_dv[db][4 * g4 + 2], acc_dv[db][4 * g4 + 3]);
-        *(uint2*)(dvp + db * 32 + 8 * g4 + 4 * hi) = w;
-        w.x = pack_bf16x2(acc_dk[db][4 * g4] * p.scale, acc_dk[db][4 * g4 + 1] * p.scale);
-        w.y = pack_bf16x2(acc_dk[db][4 * g4 + 2] * p.scale, acc_dk[db][4 * g4 + 3] * p.scale);
-        *(uint2*)(dkp + db * 32 + 8 * g4 + 4 * hi) = w;
-      }
+    for (int db = 0; db < D / 32; ++db) {
+      store_row_bf16x32(dvp + db * 32, acc_dv[db], 1.f, hi);
+      store_row_bf16x32(dkp + db * 32, acc_dk[db], p.scale, hi);
+    }
   }
 }
 

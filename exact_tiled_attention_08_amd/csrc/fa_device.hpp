@@ -74,6 +74,33 @@ __device__ __forceinline__ bf16x8 pack_bf16x8_sum(const float* x, float& sum) {
   return p;
 }
 
+// One row of a transposed 32 x 32 accumulator tile (lane pair l, l+32: the
+// pair's row; register r: column 8*(r/4) + 4*(l/32) + r%4), scaled by `mul`,
+// stored as 32 bf16 with 16-byte stores.  Each lane holds four-column groups;
+// one v_permlane32_swap per packed register hands a lane's second group to
+// its partner and takes the partner's first, so lane l (l < 32) stores columns
+// 16k .. 16k+7 and lane l+32 columns 16k+8 .. 16k+15 of each 16-column half k.
+// Both lanes of a pair must execute it.
+__device__ __forceinline__ void store_row_bf16x32(uint16_t* dst, const f32x16& acc, float mul, int hi) {
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t x0 = pack_bf16x2(acc[8 * k] * mul, acc[8 * k + 1] * mul);
+    const uint32_t x1 = pack_bf16x2(acc[8 * k + 2] * mul, acc[8 * k + 3] * mul);
+    const uint32_t y0 = pack_bf16x2(acc[8 * k + 4] * mul, acc[8 * k + 5] * mul);
+    const uint32_t y1 = pack_bf16x2(acc[8 * k + 6] * mul, acc[8 * k + 7] * mul);
+    // lanes < 32 keep x and receive the partner's x; lanes >= 32 keep y and
+    // receive the partner's y
+    const auto r0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+    const auto r1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+    uint4 w;
+    w.x = (uint32_t)r0[0];
+    w.y = (uint32_t)r1[0];
+    w.z = (uint32_t)r0[1];
+    w.w = (uint32_t)r1[1];
+    *(uint4*)(dst + 16 * k + 8 * hi) = w;
+  }
+}
+
 // Transposed 4 x 16 read of a row-major bf16 tile in LDS (see header note).
 __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;

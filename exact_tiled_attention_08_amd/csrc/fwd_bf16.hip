@@ -310,14 +310,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     const float inv = lt > 0.f ? 1.f / lrt : 0.f;
     uint16_t* op = p.o + (q_base + qrow) * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint2 w;
-        w.x = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
-        w.y = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-        *(uint2*)(op + db * 32 + 8 * g + 4 * hi) = w;
-      }
+    for (int db = 0; db < D / 32; ++db) store_row_bf16x32(op + db * 32, oacc[db], inv, hi);
     if (hi == 0) p.lse[q_base + qrow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
   }
 }
@@ -739,14 +732,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const float inv = lt > 0.f ? 1.f / lrt : 0.f;
       uint16_t* op = p.o + (q_base + qrow) * D;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint2 w;
-          w.x = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
-          w.y = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-          *(uint2*)(op + db * 32 + 8 * g + 4 * hi) = w;
-        }
+      for (int db = 0; db < D / 32; ++db) store_row_bf16x32(op + db * 32, oacc[db], inv, hi);
       if (hi == 0) p.lse[q_base + qrow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
     }
   }
