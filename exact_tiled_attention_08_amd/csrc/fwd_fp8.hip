@@ -15,11 +15,12 @@
 //     the sum of |products|), which bounds the score error by that fraction of
 //     scale * sum_d |q_d k_d|.
 //   * K tiles stay FP8 in LDS (8 KiB per 64 keys, half the bytes).
-//   * V is converted exactly to bf16 while it is staged (every E4M3 and E5M2
-//     value is a bf16 value), and O^T += V^T P^T stays on the bf16 matrix
-//     cores with P rounded to bf16, exactly as in the bf16 kernel; v's
-//     descale multiplies O once at the end.  P itself is never quantised to
-//     FP8, so the only rounding that FP8 adds is the caller's own.
+//   * V is converted exactly to bf16 while it is staged, in the matrix phase
+//     (every E4M3 and E5M2 value is a bf16 value), and O^T += V^T P^T stays
+//     on the bf16 matrix cores with P rounded to bf16, exactly as in the bf16
+//     kernel; v's descale multiplies O once at the end.  P itself is never
+//     quantised to FP8, so the only rounding that FP8 adds is the caller's
+//     own.
 // Everything else -- grid, heaviest-first order, two 4-wave groups one phase
 // apart, three rotating buffers, masks, lazy rescale, epilogue -- is the
 // bf16 kernel's.
@@ -324,13 +325,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     lr += (lrp[0] + lrp[1]) + (lrp[2] + lrp[3]);
   };
 
-  // Each step issues one K copy (matrix phase) and one V load (softmax
-  // phase) per thread.  The V load of step j-1 (tile j+1) is converted into
-  // LDS in the softmax phase of step j; the compiler's own wait for it also
-  // covers that step's K copy.  Before either barrier of step j every wave
-  // leaves at most two memory operations in flight: the K copy of step j-1
-  // (tile j+1, read from phase 2j+2 on) is then complete by the barrier that
-  // ends phase 2j+1, as in the bf16 kernel.
+  // Each step issues one V load and one K copy per thread, both in the
+  // matrix phase after its products are issued (the vector ALU has room
+  // there; the softmax phase is the longer one).  The V load of step j-1
+  // (tile j+1) is converted into LDS in the matrix phase of step j, into a
+  // buffer no wave reads then: it last held tile j-2, whose last reads ended
+  // before the barrier that opened the phase, and tile j+1 is first read in
+  // phase 2j+4.  The compiler's own wait for the load also covers the copies
+  // issued after it.  Before either barrier of step j every wave leaves at
+  // most two memory operations in flight (step j's own V load and K copy):
+  // the K copy of step j-1 (tile j+1, read from phase 2j+2 on) is then
+  // complete by the barrier that ends phase 2j+1, as in the bf16 kernel.
   auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
   auto wait_copies = [&]() { asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); };
 
@@ -354,12 +359,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // loop is unrolled by three so that they are constants.
     auto step = [&](int j, int b0, int b1, int b2) {
       matrix_phase(b0, b2);  // K_j in K buffer b0, V_{j-1} in V buffer b2
+      store_v(b1);           // V_{j+1} into V buffer (j + 1) % 3
+      load_v(j + 2);
       copy_k(j + 2, b2);
       wait_copies();
       barrier();
       softmax_phase(j);
-      store_v(b1);           // V_{j+1} into V buffer (j + 1) % 3
-      load_v(j + 2);
       wait_copies();
       barrier();
     };
