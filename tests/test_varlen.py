@@ -138,3 +138,22 @@ def test_varlen_full_size_sampled():
         hk = h // 4
         O_ref, L_ref = oracle.attention_varlen_ref(q[h:h + 1], k[hk:hk + 1], v[hk:hk + 1], cu_q, cu_k, causal=True)
         compare(o[h:h + 1], lse[h:h + 1], O_ref, L_ref, torch.bfloat16, f"varlen full size head {h}")
+
+
+@pytest.mark.gpu
+@pytest.mark.slow
+@pytest.mark.parametrize("chunked", [False, True])
+def test_varlen_d64_causal_on_a_large_grid(chunked):
+    """d = 64 under a causal mask with enough heads that the packed grid has
+    two 256-row work-groups per CU (the ping-pong kernel; the small d = 64
+    cases above take the 128-row kernel): Hq=64, Hkv=16, four sequences,
+    self-attention or 300-query chunks against their keys; four heads compared
+    with the oracle, every row."""
+    lens_k = [1500, 2048, 901, 1777]
+    lens_q = [300, 300, 300, 300] if chunked else lens_k
+    q, k, v, cu_q, cu_k = inputs.make_packed(2, lens_q, lens_k, 64, 16, 64)
+    o, lse = run_varlen(q, k, v, cu_q, cu_k, True)
+    for h in (0, 17, 42, 63):
+        hk = h // 4
+        O_ref, L_ref = oracle.attention_varlen_ref(q[h:h + 1], k[hk:hk + 1], v[hk:hk + 1], cu_q, cu_k, causal=True)
+        compare(o[h:h + 1], lse[h:h + 1], O_ref, L_ref, torch.bfloat16, f"varlen d=64 large grid head {h}")
