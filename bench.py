@@ -16,7 +16,9 @@ matrix-core-only loop on random operands (the denominator the kernels are
 read against: on random data the chip sustains a lower clock than on the
 small constants of the same loop, which is timed too) and a streaming read.  The other workloads (d=64
 self-attention, padded GQA, backward, FP8, packed, paged decode) are timed
-after the step as side legs, each after its own time-based warm-up.
+after the step as side legs, each after its own time-based warm-up; a last leg
+runs the headline kernel on all-zero operands, which shows how much of the
+clock the chip's power limit takes on the random inputs.
 """
 import argparse
 import hashlib
@@ -258,6 +260,11 @@ def profile_only(args, dev):
         q, k, v = [t.to(dev) for t in inputs.make_inputs(3)[:3]]
         for _ in range(n):
             fa.fa_fwd(q, k, v, causal=True)
+    elif args.only == "prefill_zero":
+        q = torch.zeros(inputs.CONFIGS[3]["B"], inputs.CONFIGS[3]["Hq"], inputs.CONFIGS[3]["Nq"],
+                        inputs.CONFIGS[3]["d"], dtype=torch.bfloat16, device=dev)
+        for _ in range(n):
+            fa.fa_fwd(q, q, q, causal=True)
     elif args.only in ("d64", "d64nc"):
         q, k, v = [t.to(dev) for t in inputs.make_inputs(2)[:3]]
         for _ in range(n):
@@ -329,8 +336,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--side-steps", type=int, default=20,
                     help="timed calls of each side leg (d=64, padded GQA, backward, paged, packed, FP8); 0 = skip")
-    ap.add_argument("--only", choices=["prefill", "d64", "d64nc", "gqa", "decode", "backward", "fp8", "varlen",
-                                       "paged", "copy", "ceilings"],
+    ap.add_argument("--only", choices=["prefill", "prefill_zero", "d64", "d64nc", "gqa", "decode", "backward", "fp8",
+                                       "varlen", "paged", "copy", "ceilings"],
                     default=None,
                     help="profiling aid: run only one part (or a 1 GiB device copy used to calibrate the HBM byte "
                          "counters, or the matrix-core ceilings) and print no JSON")
@@ -532,6 +539,23 @@ def main():
         side["prefill_fp8"] = fp8
         log(f"fp8 prefill: {fp8['value']} TFLOP/s")
         del q8, k8, v8
+
+        # ---- the headline kernel and shape on all-zero Q, K, V: the same instruction stream and
+        # schedule, but operands that toggle no bits, so the chip holds a higher clock.  A check of
+        # the power limit, not a workload: the metric above stays on the N(0,1) inputs.
+        z3 = torch.zeros_like(q3)
+        call = lambda: fa.fa_fwd(z3, z3, z3, causal=True, out=o3, lse=l3)  # noqa: E731
+        warm(call, seconds=WARM_S)
+        ms = time_calls(call, n_side, stream)
+        zero = mfma_leg(ms, f_fwd, "fwd_bf16_pp_kernel<causal>",
+                        "prefill fwd B=1 H=32 N=8192 d=128 causal bf16 on all-zero Q, K, V (power-limit check)",
+                        None, load_util("fwd_bf16_pp_kernel_zero_operands"), None)
+        zero["ratio_to_headline"] = round(zero["value"] / fwd_tflops, 4)
+        zero["note"] = ("same kernel, shape and launch as the headline on operands that toggle no bits; the "
+                        "speed-up over the N(0,1) inputs is the clock the chip's power limit takes away")
+        side["prefill_zero_operands"] = zero
+        log(f"prefill on zero operands: {zero['value']} TFLOP/s")
+        del z3
 
     rec = {
         "metric": METRIC,
