@@ -258,8 +258,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 //   dV^T += dO^T P  (A: transposed reads of dO),  dK^T += Q^T dS  (A: Q^T)
 // The Q and dO tiles rotate through two LDS buffers, filled by direct
 // global->LDS copies one tile ahead (rows past the sequence re-read its last
-// row: their LSE is +inf, so they carry no weight); wave 0 stages each tile's
-// LSE and row dots.  One barrier per tile (tests/test_schedule_model.py
+// row: their LSE is +inf, so they carry no weight); waves 0 and 1 stage each
+// tile's LSE and row dots.  One barrier per tile (tests/test_schedule_model.py
 // replays the schedule).  The per-lane LDS offsets are computed once and the
 // (head, query tile) walk advances by counters, so a tile costs no divisions.
 // 64.5 KiB of LDS and at most 256 VGPRs, so two work-groups share a CU.
@@ -336,18 +336,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       copy_tile_rows<D>(p.q + rb * D, q0, p.Nq, c, lds + q_off(buf), lane);
       copy_tile_rows<D>(p.dout + rb * D, q0, p.Nq, c, lds + do_off(buf), lane);
     }
-    // wave 0 loads the tile's LSE (lanes 0..31) and row dots (lanes 32..63)
-    float r = 0.f;
-    if (wave_u == 0) {
-      const int q = q0 + li;
-      if (hi == 0) r = q < p.Nq ? lse_base2(p.lse[rb + q]) : __builtin_inff();
-      else r = q < p.Nq ? p.rowdot[rb + q] : 0.f;
-    }
     if (++next_qt == n_qt) {
       next_qt = qt_first;
       ++next_h;
     }
-    return r;
+  };
+  // The row data of the tile (next_h, next_qt), as stored: even waves load
+  // the LSE, odd waves the row dots (a wave-uniform choice), one row per lane
+  // (rows past the query count, and the tile after the last one, re-read a
+  // valid row).  Waves 0 and 1 put them in LDS after the tile's wait for its
+  // copies.  The loaded value is read nowhere before that wait, so no wait
+  // the compiler places for it falls inside the tile, where it would also
+  // wait for the copies just issued.
+  int ld_q = 0;  // row of the lane's loaded value (for the validity test)
+  auto ld_load = [&]() {
+    const int hq = hk * group + min(next_h, group - 1);
+    ld_q = next_qt * BQ + li;
+    const float* src = (wave_u & 1) ? p.rowdot : p.lse;
+    return src[((size_t)b * p.Hq + hq) * (size_t)p.Nq + min(ld_q, p.Nq - 1)];
+  };
+  // LDS slot of a tile's row li: the LSE in base 2 (+inf for a row with no
+  // visible key or past the query count: every P of the row is then 0), or
+  // the row dot (0 past the query count).
+  auto ld_store = [&](int buf, float raw) {
+    if (wave_u < 2 && hi == 0) {
+      const bool ok = ld_q < p.Nq;
+      ld_lds[buf][wave_u][li] = wave_u == 0 ? (ok ? lse_base2(raw) : __builtin_inff()) : (ok ? raw : 0.f);
+    }
   };
 
   // B operand of S: lane (li, hi) holds K of key `key`, columns 16*st + 8*hi .. +7
@@ -368,15 +383,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint16_t* vsrc = p.v + kv_base * D;
 #pragma unroll
     for (int i = 0; i < VCOPIES; ++i) copy_tile_rows<D>(vsrc, kt0, kv_len, wave_u * VCOPIES + i, lds + V_OFF, lane);
-    ld_reg = issue_next(0);
+    ld_reg = ld_load();
+    issue_next(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (wave_u == 0) ld_lds[0][hi][li] = ld_reg;
+    ld_store(0, ld_reg);
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   int cur_qt = qt_first;  // query tile being computed
   auto tile = [&](int it, int buf) {
-    if (it + 1 < n_it) ld_reg = issue_next(buf ^ 1);
+    ld_reg = ld_load();
+    if (it + 1 < n_it) issue_next(buf ^ 1);
     const int q0 = cur_qt * BQ;
     if (++cur_qt == n_qt) cur_qt = qt_first;
     // Tiles whose queries all see every key of the wave skip the mask.
@@ -445,7 +462,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     grads(1, pack_bf16x8(pv), pack_bf16x8(dsv));
 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next tile's copies and LSE/row dots
-    if (wave_u == 0 && it + 1 < n_it) ld_lds[buf ^ 1][hi][li] = ld_reg;
+    if (it + 1 < n_it) ld_store(buf ^ 1, ld_reg);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
   for (int it = 0; it < n_it; ++it) tile(it, it & 1);
