@@ -113,11 +113,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   const int wave = tid >> 6, lane = tid & 63;
   const int li = lane & 31, hi = lane >> 5;
 
-  // Work-group -> (query tile, head, batch).  The last (heaviest, under a
-  // causal mask) query tiles of every head are dispatched first.
+  // Work-group -> (query tile, head, batch).  The heavier half of the query
+  // tiles (under a causal mask, the last ones) is dispatched first, heaviest
+  // first; the lighter half follows lightest first, so that the work-groups
+  // dispatched one grid-half apart, which share a CU when the whole grid is
+  // resident at once (this kernel runs small causal grids), carry about the
+  // same work together: tiles n-1-s and s.
   const int bh_count = p.B * p.Hq;
   const int bh = xcd_grouped_head((int)(blockIdx.x % bh_count), p.B, p.Hq, p.Hkv);
-  const int qt = p.n_qtiles - 1 - (int)(blockIdx.x / bh_count);
+  const int slot = (int)(blockIdx.x / bh_count), half = (p.n_qtiles + 1) / 2;
+  const int qt = !CAUSAL ? p.n_qtiles - 1 - slot : (slot < half ? p.n_qtiles - 1 - slot : slot - half);
   const int b = bh / p.Hq, hq = bh - b * p.Hq;
   const int hk = hq / (p.Hq / p.Hkv);
 
