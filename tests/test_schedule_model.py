@@ -752,3 +752,26 @@ def test_head_mapping_is_a_permutation_grouped_by_xcd(B, Hq, Hkv):
                 kv_group = b * Hkv + hq // g
                 assert kv_group % 8 == block % 8, (B, Hq, Hkv, block)  # same XCD for a KV head's heads
         assert sorted(heads) == list(range(bh_count))
+
+
+# ---------------------------------------------------------------------------
+# The 128-row causal kernel's dispatch order (fwd_bf16_kernel): query-tile
+# slot s -> tile n-1-s for the first half of the slots, s-half for the rest, so
+# that slots s and s+half (one grid-half apart, co-resident on a CU when the
+# whole grid fits) carry tiles n-1-s and s, whose causal work adds up to the
+# same for every s.
+def causal_slot_tile(slot, n):
+    half = (n + 1) // 2
+    return n - 1 - slot if slot < half else slot - half
+
+
+@pytest.mark.parametrize("n", list(range(1, 41)))
+def test_causal_dispatch_order_is_a_permutation_pairing_heavy_with_light(n):
+    tiles = [causal_slot_tile(s, n) for s in range(n)]
+    assert sorted(tiles) == list(range(n))
+    half = (n + 1) // 2
+    # the first half is heaviest first
+    assert tiles[:half] == sorted(tiles[:half], reverse=True)
+    # slot s and slot s+half hold tiles n-1-s and s: the same sum for every s
+    sums = {tiles[s] + tiles[s + half] for s in range(n - half)}
+    assert sums <= {n - 1}
